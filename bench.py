@@ -1,0 +1,283 @@
+"""Benchmark of the paged-attention decode hot path on one MI355X.
+
+A step is one pass of the hot path over one batch: reshape_and_cache of the
+batch's new K/V tokens, then paged_attention_decode over every sequence (and,
+for the long mixed workload, paged_attention_chunked).  Inputs are seeded and
+synthetic and resident in HBM before timing starts.
+
+Default workload: GQA decode, 32 query / 8 kv heads, head_dim 128, bf16,
+block 16, 256 sequences with lognormal context lengths (median 1024, sigma 1,
+clipped to [16, 8192]).  The metric is the algorithmic KV+Q bytes read per
+second (every logical token's K and V for every kv head once, plus the
+queries), with sequences per second alongside.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload gqa|opt13b|long]
+"""
+
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import re
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "paged-attn decode achieved HBM GB/s (% of MI355X peak) + sequences/sec"
+PEAK_HBM_GBS = 8000.0
+PROFILES = os.path.join(ROOT, "profiles")
+KERNEL_SOURCE = os.path.join(ROOT, "paged_kv_cache_265_amd", "csrc", "decode.hip")
+
+
+def log(msg):
+    print(msg, file=sys.stderr, flush=True)
+
+
+def source_sha() -> str:
+    return hashlib.sha256(open(KERNEL_SOURCE, "rb").read()).hexdigest()[:16]
+
+
+def traffic_from_profiles(workload: str):
+    """HBM bytes per decode launch from the committed counter summary, if it was
+    taken on the current kernel source; else None."""
+    path = os.path.join(PROFILES, f"decode_{workload}_traffic.md")
+    if not os.path.exists(path):
+        return None
+    text = open(path).read()
+    sha = re.search(r"source_sha256_16:\s*([0-9a-f]+)", text)
+    val = re.search(r"hbm_bytes_per_launch:\s*([0-9.eE+]+)", text)
+    if not sha or not val or sha.group(1) != source_sha():
+        return None
+    return float(val.group(1))
+
+
+def build_workload(name: str):
+    import workloads
+    if name == "gqa":
+        c = workloads.config_decode(3)
+        return {"decode": c, "new": (c.new_key, c.new_value, c.slot_mapping), "partition_size": 0,
+                "config": {"workload": "GQA decode 32 q heads / 8 kv heads, head_dim 128, bf16, block 16, "
+                                       "256 seqs, context lognormal(median 1024, sigma 1) clipped to [16, 8192], "
+                                       "plus reshape_and_cache of 256 new tokens",
+                           "num_seqs": c.num_seqs, "num_q_heads": 32, "num_kv_heads": 8, "head_dim": 128,
+                           "block_size": 16, "total_context_tokens": int(c.context_lens.sum()),
+                           "max_context": int(c.context_lens.max()), "parallelism": "none (one GPU)"}}
+    if name == "opt13b":
+        c = workloads.config_decode(2)
+        return {"decode": c, "new": None, "partition_size": 0,
+                "config": {"workload": "OPT-13B-shaped layer decode, 40 heads MHA, head_dim 128, fp16, block 16, "
+                                       "64 seqs, context uniform [128, 2048]",
+                           "num_seqs": 64, "total_context_tokens": int(c.context_lens.sum())}}
+    raise ValueError(name)
+
+
+def build_long():
+    import workloads
+    p, qd, qc, cu = workloads.config_long_mixed()
+    return p, qd, qc, cu
+
+
+def cpu_baseline(case, budget_s: float = 20.0):
+    """The fp64 oracle on a bounded sample of the same batch (the first k sequences),
+    timed on this host's cores."""
+    import oracle
+    import workloads
+    threads = int(os.environ.get("OMP_NUM_THREADS", os.cpu_count() or 1))
+    order = list(range(case.num_seqs))
+    k = 8
+    spent = 0.0
+    done = 0
+    bytes_done = 0
+    while done < len(order) and spent < budget_s:
+        sel = order[done:done + k]
+        t0 = time.perf_counter()
+        oracle.decode(case.query[sel], case.pool.key_cache, case.pool.value_cache, case.block_tables[sel],
+                      case.context_lens[sel], case.num_kv_heads, case.block_size, case.scale, case.dtype)
+        spent += time.perf_counter() - t0
+        bytes_done += workloads.algorithmic_decode_bytes(case.context_lens[sel], case.num_q_heads,
+                                                         case.num_kv_heads, case.head_dim,
+                                                         workloads.DTYPES[case.dtype][2])
+        done += len(sel)
+        k = min(2 * k, 64)
+    return {"value": bytes_done / spent / 1e9, "unit": "GB/s", "cores": threads, "kind": "oracle",
+            "sample": f"first {done} of {case.num_seqs} sequences of the same batch "
+                      f"({int(case.context_lens[:done].sum())} context tokens), fp64 C oracle, "
+                      f"{spent:.1f} s wall", "seqs_per_s": done / spent}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", default="gqa", choices=["gqa", "opt13b", "long"])
+    ap.add_argument("--partition-size", type=int, default=None)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="time a plain 1 GiB device copy (reference kernel for the HBM counters)")
+    args = ap.parse_args()
+
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print(json.dumps({"error": "this build runs on exactly one GPU: the decode hot path has no multi-GPU "
+                                   "leg here (sequences would shard across GPUs with no exchange); run with "
+                                   "--gpus 1"}))
+        sys.exit(2)
+
+    import torch
+    import paged_kv_cache_265_amd as pkv
+    import workloads
+
+    assert torch.cuda.is_available(), "needs a GPU"
+    pkv.load_library()
+    dev = torch.device("cuda:0")
+
+    if args.copy_calibration:
+        n = 1 << 30
+        a = torch.empty(n, dtype=torch.uint8, device=dev)
+        b = torch.empty_like(a)
+        for _ in range(5):
+            b.copy_(a)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_calibration_bytes": n, "launches": 5}))
+        return
+
+    t_gen = time.perf_counter()
+    if args.workload == "long":
+        p, qd, qc, cu = build_long()
+        run = run_long(args, p, qd, qc, cu, torch, pkv, workloads, dev)
+        return run
+    W = build_workload(args.workload)
+    case = W["decode"]
+    part = W["partition_size"] if args.partition_size is None else args.partition_size
+    log(f"generated {args.workload} in {time.perf_counter() - t_gen:.1f} s; moving to the GPU")
+
+    kc = case.pool.key_cache.to(dev)
+    vc = case.pool.value_cache.to(dev)
+    q = case.query.to(dev)
+    bt = torch.from_numpy(case.block_tables).to(dev)
+    cl = torch.from_numpy(case.context_lens).to(dev)
+    out = torch.empty_like(q)
+    ws_bytes = pkv.decode_workspace_size(case.num_seqs, case.num_q_heads, case.num_kv_heads, case.head_dim,
+                                         case.block_size, case.max_blocks_per_seq, part)
+    ws = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=dev)
+    new = None
+    if W["new"] is not None:
+        nk, nv, sm = W["new"]
+        new = (nk.to(dev), nv.to(dev), torch.from_numpy(sm).to(dev))
+    torch.cuda.synchronize()
+
+    def step(ev=None):
+        if new is not None:
+            pkv.reshape_and_cache(new[0], new[1], kc, vc, new[2])
+        if ev is not None:
+            ev[0].record()
+        pkv.paged_attention_decode(out, q, kc, vc, bt, cl, case.scale, partition_size=part, workspace=ws)
+        if ev is not None:
+            ev[1].record()
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(evs[i])
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    ms_step = (t1 - t0) * 1e3 / args.steps
+    dec_ms = float(np.mean([a.elapsed_time(b) for a, b in evs]))
+
+    eb = workloads.DTYPES[case.dtype][2]
+    nbytes = workloads.algorithmic_decode_bytes(case.context_lens, case.num_q_heads, case.num_kv_heads,
+                                                case.head_dim, eb)
+    value = nbytes / (ms_step * 1e-3) / 1e9
+    achieved = nbytes / (dec_ms * 1e-3) / 1e9
+    traffic = traffic_from_profiles(args.workload)
+    res = {
+        "metric": METRIC, "value": round(value, 1), "unit": "GB/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(ms_step, 4), "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": case.dtype, "data": "synthetic (seeded N(0,1) K/V/q, shuffled block placement)",
+        "config": W["config"],
+        "pct_of_peak": round(100.0 * value / PEAK_HBM_GBS, 2),
+        "seqs_per_s": round(case.num_seqs / (ms_step * 1e-3), 1),
+        "algorithmic_bytes_per_step": nbytes,
+        "partition_size": pkv.decode_partition_size(case.num_seqs, case.num_q_heads, case.num_kv_heads,
+                                                    case.head_dim, case.block_size, case.max_blocks_per_seq, part),
+        "roofline": {"bound": "hbm", "kernel": "paged_attention_decode (decode kernel + partition merge)",
+                     "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                     "frac": round(achieved / PEAK_HBM_GBS, 4), "avg_call_ms": round(dec_ms, 4),
+                     "traffic": traffic},
+    }
+    if not args.no_cpu_baseline:
+        log("timing the CPU oracle on a bounded sample")
+        res["cpu_baseline"] = cpu_baseline(case)
+    print(json.dumps(res), flush=True)
+
+
+def run_long(args, p, qd, qc, cu, torch, pkv, workloads, dev):
+    S = qd.shape[0]
+    kc = p.pool.key_cache.to(dev)
+    vc = p.pool.value_cache.to(dev)
+    q = qd.to(dev)
+    qcd = qc.to(dev)
+    cud = torch.from_numpy(cu).to(dev)
+    bt = torch.from_numpy(p.block_tables).to(dev)
+    cl = torch.from_numpy(p.context_lens).to(dev)
+    pend = np.nonzero(p.pending)[0]
+    nk = p.logical_k[torch.from_numpy(pend)].to(dev)
+    nv = p.logical_v[torch.from_numpy(pend)].to(dev)
+    sm = torch.from_numpy(p.token_slots[pend]).to(dev)
+    out = torch.empty_like(q)
+    outc = torch.empty_like(qcd)
+    ws = torch.empty(pkv.decode_workspace_size(S, 32, 1, 128, 16, p.block_tables.shape[1], 512), dtype=torch.uint8,
+                     device=dev)
+    scale = 1.0 / np.sqrt(128)
+    torch.cuda.synchronize()
+
+    def step(ev=None):
+        pkv.reshape_and_cache(nk, nv, kc, vc, sm)
+        if ev is not None:
+            ev[0].record()
+        pkv.paged_attention_decode(out, q, kc, vc, bt[:S], cl[:S], scale, partition_size=512, workspace=ws)
+        if ev is not None:
+            ev[1].record()
+        pkv.paged_attention_chunked(outc, qcd, cud, 512, kc, vc, bt[S:], cl[S:], scale)
+        if ev is not None:
+            ev[2].record()
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    evs = [tuple(torch.cuda.Event(enable_timing=True) for _ in range(3)) for _ in range(args.steps)]
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(evs[i])
+    torch.cuda.synchronize()
+    ms_step = (time.perf_counter() - t0) * 1e3 / args.steps
+    dec_ms = float(np.mean([a.elapsed_time(b) for a, b, c in evs]))
+    chk_ms = float(np.mean([b.elapsed_time(c) for a, b, c in evs]))
+    nbytes = workloads.algorithmic_decode_bytes(p.context_lens[:S], 32, 1, 128, 2)
+    flops = workloads.algorithmic_chunked_flops(p.context_lens[S:], np.diff(cu), 32, 128)
+    res = {"metric": METRIC, "value": round(nbytes / (dec_ms * 1e-3) / 1e9, 1), "unit": "GB/s", "n_gpus": 1,
+           "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_step, 4), "higher_is_better": True,
+           "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+           "config": {"workload": "long-context mixed batch: MQA 32/1 decode of 32 seqs (context uniform "
+                                  "[16384, 131072], 512-token partitions) + 8 chunked-prefill segments of 512 "
+                                  "rows over 4096 cached tokens"},
+           "decode_ms": round(dec_ms, 4), "chunked_ms": round(chk_ms, 4),
+           "chunked_tflops": round(flops / (chk_ms * 1e-3) / 1e12, 2),
+           "roofline": {"bound": "hbm", "kernel": "paged_attention_decode", "achieved":
+                        round(nbytes / (dec_ms * 1e-3) / 1e9, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                        "frac": round(nbytes / (dec_ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4), "traffic": None}}
+    print(json.dumps(res), flush=True)
+
+
+if __name__ == "__main__":
+    main()

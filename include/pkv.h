@@ -1,0 +1,181 @@
+/*
+ * pkv.h -- C ABI of the paged-attention library for AMD Instinct MI355X (gfx950).
+ *
+ * Four calls make up the hot path of decoding over a paged KV cache:
+ *   paged_attention_decode   one query token per sequence over its paged K/V
+ *   paged_attention_chunked  causal attention of short query chunks (chunked prefill)
+ *   reshape_and_cache        write new K/V tokens into their slots
+ *   copy_blocks              whole-block copies for copy-on-write
+ *
+ * Sources.  The operation is the one described on three web pages:
+ *  [P1] "每生成一个字都要把全部权重读一遍：从 vLLM 看 LLM 推理提速" -- section on paging
+ *       the KV cache: fixed-size blocks placed anywhere in a physical pool, a
+ *       per-sequence block table, the blockwise attention equation
+ *       s_j = q.K_j / sqrt(d_k), o = sum_j softmax(s)_j V_j (equal to attention over
+ *       the blocks concatenated in logical order), and copy-on-write of a shared
+ *       block with a reference count.
+ *  [P2] "现代 LLM 推理引擎剖析" -- section 1.3 (block size 16 by default; block bytes
+ *       2 x block_size x kv heads x head size x dtype bytes), section 1.6 (slot_mapping
+ *       built when preparing inputs; custom paged-attention kernel over a
+ *       flattened batch), section 2.1 (chunked prefill).
+ *  [P3] "LLM 推理优化的系统视角：从 KV Cache 到调度" -- section 3.1 (dense causal
+ *       attention; a decode step reads the cached K/V and appends the new one),
+ *       section 4.1 (MHA / MQA / GQA: a group of query heads shares one K/V head).
+ *
+ * ---------------------------------------------------------------------------------
+ * Memory layout (all device memory, row-major, no padding).  Notation:
+ *   S  = num_seqs, Hq = num_q_heads, Hkv = num_kv_heads, G = Hq / Hkv,
+ *   D  = head_dim, BS = block_size, NB = num_blocks, MB = max_blocks_per_seq.
+ *   query        [S][Hq][D]           (decode)  or [total_q][Hq][D] (chunked)
+ *   out          same shape and type as query
+ *   key_cache    [NB][Hkv][BS][D]     one (block, kv head) tile is token-major
+ *   value_cache  [NB][Hkv][D][BS]     one (block, kv head) tile is head_dim-major
+ *   block_tables int32 [rows][MB]     physical block of each logical block; entries
+ *                                     at index >= ceil(ctx / BS) are never read
+ *   context_lens int32 [rows]         tokens of each sequence, including the ones
+ *                                     being decoded (write first, then attend)
+ *   slot_mapping int64 [num_tokens]   slot = block * BS + offset; negative = skip
+ * Query head h uses kv head h / G (contiguous groups; G = 1 is MHA, Hkv = 1 is MQA).
+ * The value tile is stored transposed so that the token dimension of the P.V
+ * product is contiguous.
+ *
+ * Element types: PKV_F32, PKV_F16 (IEEE binary16), PKV_BF16 (bfloat16).  Query,
+ * caches and output share one type.  Arithmetic is fp32; outputs are rounded to
+ * the element type with round-to-nearest-even.
+ *
+ * Supported: head_dim in {64, 128}, block_size == 16, Hq % Hkv == 0, Hkv >= 1.
+ *
+ * Conventions for every call:
+ *  - Ownership: the caller owns every buffer, the workspace included.  The library
+ *    allocates, frees and synchronises nothing and keeps no state besides a
+ *    thread-local error message.
+ *  - Asynchrony: calls enqueue kernels on `stream` (a hipStream_t; NULL = the null
+ *    stream) and return.  Results are ready when the stream reaches that point.
+ *  - Errors: arguments are validated on the host before anything is launched; an
+ *    invalid argument returns a negative code and launches nothing.  A launch
+ *    failure returns PKV_ERR_HIP.  pkv_last_error() gives a message.
+ *  - Device-side contract (not checked): block ids in tables and block_mapping are
+ *    in [0, NB); context_lens[i] <= MB * BS; slots are unique and < NB * BS; the
+ *    copy_blocks destination set has no duplicates and is disjoint from its
+ *    source set; outputs do not alias inputs.  Breaking it reads or writes out of
+ *    bounds.
+ *  - Pointers to query/out/caches/key/value must be 16-byte aligned.
+ */
+#ifndef PKV_H
+#define PKV_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+enum pkv_dtype { PKV_F32 = 0, PKV_F16 = 1, PKV_BF16 = 2 };
+
+enum pkv_status {
+    PKV_OK = 0,
+    PKV_ERR_INVALID = -1,     /* null pointer, bad size, Hq % Hkv != 0, bad scale, misaligned pointer */
+    PKV_ERR_UNSUPPORTED = -2, /* head_dim, block_size or dtype outside the supported set */
+    PKV_ERR_WORKSPACE = -3,   /* workspace missing or smaller than pkv_decode_workspace_size() */
+    PKV_ERR_HIP = -4          /* the HIP runtime refused a launch */
+};
+
+/* Library version as major * 10000 + minor * 100 + patch. */
+int pkv_version(void);
+
+/* Partition length (tokens) that paged_attention_decode uses for the given
+ * arguments: partition_size itself when > 0, else the library's choice (a
+ * multiple of block_size that depends only on these host scalars).  Returns a
+ * negative status on invalid arguments. */
+int pkv_decode_partition_size(int num_seqs, int num_q_heads, int num_kv_heads, int head_dim, int block_size,
+                              int max_blocks_per_seq, int partition_size);
+
+/* Bytes of workspace paged_attention_decode needs.  Zero when every sequence fits
+ * one partition (max_blocks_per_seq * block_size <= partition length).  Returns 0
+ * on invalid arguments as well; the decode call then reports the error. */
+size_t pkv_decode_workspace_size(int num_seqs, int num_q_heads, int num_kv_heads, int head_dim, int block_size,
+                                 int max_blocks_per_seq, int partition_size);
+
+/*
+ * paged_attention_decode -- [P1] blockwise attention equation; [P3] section 3.1.
+ *
+ * For each sequence s and query head h (kv head g = h / G), with n = context_lens[s]:
+ *   K_t = key_cache[block_tables[s][t / BS]][g][t % BS][:], V_t likewise from
+ *   value_cache[...][g][:][t % BS], for t = 0 .. n-1;
+ *   out[s][h][:] = sum_t exp(x_t - max x) V_t / sum_t exp(x_t - max x),
+ *   x_t = scale * (query[s][h][:] . K_t).
+ * The softmax is one softmax over all n tokens.  n = 0 gives a zero output.
+ *
+ * Long contexts are split into partitions of pkv_decode_partition_size() tokens;
+ * each partition keeps (running max, running sum, unnormalised output) in the
+ * workspace and a second kernel merges them.
+ *   workspace / workspace_bytes: device buffer of at least
+ *   pkv_decode_workspace_size(...) bytes (may be NULL when that size is 0).  Its
+ *   contents on entry do not matter and are undefined on return.
+ *   partition_size: 0 = library choice, else a positive multiple of block_size.
+ */
+int paged_attention_decode(void* out, const void* query, const void* key_cache, const void* value_cache,
+                           const int32_t* block_tables, const int32_t* context_lens, int num_seqs,
+                           int num_q_heads, int num_kv_heads, int head_dim, int block_size, int num_blocks,
+                           int max_blocks_per_seq, float scale, int dtype, int partition_size, void* workspace,
+                           size_t workspace_bytes, void* stream);
+
+/*
+ * paged_attention_chunked -- [P2] sections 1.4 and 2.1 (a long prompt is cut into
+ * chunks that run in a flattened batch); [P3] section 3.1 (causal attention).
+ *
+ * Segment i owns query rows cu_q_lens[i] .. cu_q_lens[i+1]-1 (L_i rows) and has
+ * n_i = context_lens[i] tokens in the cache, its own chunk included (write the
+ * chunk with reshape_and_cache first).  Row r of segment i sits at position
+ * n_i - L_i + r and attends to tokens 0 .. n_i - L_i + r through block_tables[i].
+ *   cu_q_lens: device int32 [num_segs + 1], cu_q_lens[0] = 0, non-decreasing,
+ *              cu_q_lens[num_segs] = total_q.
+ *   max_q_len: host bound on every L_i (sizes the grid; rows beyond L_i are idle).
+ * Requires context_lens[i] >= L_i (device contract).
+ */
+int paged_attention_chunked(void* out, const void* query, const int32_t* cu_q_lens, int num_segs, int total_q,
+                            int max_q_len, const void* key_cache, const void* value_cache,
+                            const int32_t* block_tables, const int32_t* context_lens, int num_q_heads,
+                            int num_kv_heads, int head_dim, int block_size, int num_blocks, int max_blocks_per_seq,
+                            float scale, int dtype, void* stream);
+
+/*
+ * reshape_and_cache -- [P2] section 1.6 (slot_mapping); [P3] section 3.1 (append the
+ * new K/V to the cache).
+ *
+ * For token i with slot = slot_mapping[i] >= 0, b = slot / BS, o = slot % BS:
+ *   key_cache[b][h][o][:] = key[i][h][:] and value_cache[b][h][:][o] = value[i][h][:]
+ * for every kv head h.  A bit copy: no conversion, no rounding.
+ *   key, value: device [num_tokens][Hkv][D].  num_tokens may be 0.
+ */
+int reshape_and_cache(const void* key, const void* value, void* key_cache, void* value_cache,
+                      const int64_t* slot_mapping, int num_tokens, int num_kv_heads, int head_dim, int block_size,
+                      int num_blocks, int dtype, void* stream);
+
+/*
+ * copy_blocks -- [P1] copy-on-write paragraph (a block shared by several sequences is
+ * copied whole before one of them writes into it).
+ *
+ * For every layer l < num_layers and pair p < num_pairs with (src, dst) =
+ * (block_mapping[2p], block_mapping[2p+1]): block dst of key_caches[l] and of
+ * value_caches[l] becomes a bit copy of block src.
+ *   key_caches, value_caches: HOST arrays of num_layers device pointers, each a
+ *                             pool laid out as above.
+ *   block_mapping: device int64 [num_pairs][2].  num_pairs and num_layers may be 0.
+ */
+int copy_blocks(void* const* key_caches, void* const* value_caches, int num_layers, const int64_t* block_mapping,
+                int num_pairs, int num_kv_heads, int head_dim, int block_size, int num_blocks, int dtype,
+                void* stream);
+
+/* Fixed text for a status code. */
+const char* pkv_error_string(int status);
+
+/* Message of the last failed call on this thread ("" if none). */
+const char* pkv_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* PKV_H */

@@ -1,0 +1,290 @@
+// api.cpp -- the C ABI declared in include/pkv.h: host-side validation of every
+// argument, then kernel launches on the caller's stream.  No allocation, no
+// synchronisation, no state besides a thread-local error message.
+#include "pkv.h"
+
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstdlib>
+#include <cstring>
+
+#include "internal.h"
+
+namespace {
+
+thread_local char g_msg[512] = "";
+
+int fail(int code, const char* fmt, ...) {
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(g_msg, sizeof g_msg, fmt, ap);
+    va_end(ap);
+    return code;
+}
+
+int hip_fail(hipError_t e, const char* what) {
+    return fail(PKV_ERR_HIP, "%s: launch failed: %s", what, hipGetErrorString(e));
+}
+
+bool aligned(const void* p, size_t a) { return ((uintptr_t)p & (a - 1)) == 0; }
+
+bool dtype_ok(int dt) { return dt == PKV_F32 || dt == PKV_F16 || dt == PKV_BF16; }
+
+// Checks shared by every call on the pool geometry.  Returns PKV_OK or a status.
+int check_pool(const char* fn, int num_kv_heads, int head_dim, int block_size, int num_blocks, int dtype) {
+    if (num_kv_heads <= 0) return fail(PKV_ERR_INVALID, "%s: num_kv_heads must be positive (got %d)", fn, num_kv_heads);
+    if (num_blocks <= 0) return fail(PKV_ERR_INVALID, "%s: num_blocks must be positive (got %d)", fn, num_blocks);
+    if (!dtype_ok(dtype)) return fail(PKV_ERR_UNSUPPORTED, "%s: unknown dtype %d", fn, dtype);
+    if (head_dim != 64 && head_dim != 128)
+        return fail(PKV_ERR_UNSUPPORTED, "%s: head_dim %d not supported (64 or 128)", fn, head_dim);
+    if (block_size != pkv::kBlockSize)
+        return fail(PKV_ERR_UNSUPPORTED, "%s: block_size %d not supported (16)", fn, block_size);
+    return PKV_OK;
+}
+
+int check_heads(const char* fn, int num_q_heads, int num_kv_heads) {
+    if (num_q_heads <= 0) return fail(PKV_ERR_INVALID, "%s: num_q_heads must be positive (got %d)", fn, num_q_heads);
+    if (num_q_heads % num_kv_heads != 0)
+        return fail(PKV_ERR_INVALID, "%s: num_q_heads %d is not a multiple of num_kv_heads %d", fn, num_q_heads,
+                    num_kv_heads);
+    return PKV_OK;
+}
+
+constexpr int kAutoPartition = 512;
+
+int partition_tokens(int partition_size) { return partition_size > 0 ? partition_size : kAutoPartition; }
+
+int max_parts(int max_blocks_per_seq, int part) {
+    const long long tokens = (long long)max_blocks_per_seq * pkv::kBlockSize;
+    return (int)((tokens + part - 1) / part);
+}
+
+// Decode path override for testing and measurement: PKV_DECODE_PATH=valu|mfma.
+int decode_path() {
+    const char* e = std::getenv("PKV_DECODE_PATH");
+    if (!e || !*e || !std::strcmp(e, "auto")) return 0;
+    if (!std::strcmp(e, "valu")) return 1;
+    if (!std::strcmp(e, "mfma")) return 2;
+    return -1;
+}
+
+}  // namespace
+
+extern "C" {
+
+int pkv_version(void) { return 100; }
+
+const char* pkv_error_string(int status) {
+    switch (status) {
+    case PKV_OK: return "ok";
+    case PKV_ERR_INVALID: return "invalid argument";
+    case PKV_ERR_UNSUPPORTED: return "unsupported configuration";
+    case PKV_ERR_WORKSPACE: return "workspace missing or too small";
+    case PKV_ERR_HIP: return "HIP launch failure";
+    default: return "unknown status";
+    }
+}
+
+const char* pkv_last_error(void) { return g_msg; }
+
+int pkv_decode_partition_size(int num_seqs, int num_q_heads, int num_kv_heads, int head_dim, int block_size,
+                              int max_blocks_per_seq, int partition_size) {
+    (void)num_seqs;
+    (void)num_q_heads;
+    (void)num_kv_heads;
+    (void)head_dim;
+    (void)max_blocks_per_seq;
+    if (block_size <= 0) return PKV_ERR_INVALID;
+    if (partition_size < 0 || (partition_size > 0 && partition_size % block_size != 0)) return PKV_ERR_INVALID;
+    return partition_tokens(partition_size);
+}
+
+size_t pkv_decode_workspace_size(int num_seqs, int num_q_heads, int num_kv_heads, int head_dim, int block_size,
+                                 int max_blocks_per_seq, int partition_size) {
+    const int part = pkv_decode_partition_size(num_seqs, num_q_heads, num_kv_heads, head_dim, block_size,
+                                               max_blocks_per_seq, partition_size);
+    if (part <= 0 || num_seqs <= 0 || num_q_heads <= 0 || head_dim <= 0 || max_blocks_per_seq <= 0) return 0;
+    const int mp = max_parts(max_blocks_per_seq, part);
+    if (mp <= 1) return 0;
+    return (size_t)num_seqs * num_q_heads * mp * ((size_t)head_dim * sizeof(float) + sizeof(float2));
+}
+
+int paged_attention_decode(void* out, const void* query, const void* key_cache, const void* value_cache,
+                           const int32_t* block_tables, const int32_t* context_lens, int num_seqs,
+                           int num_q_heads, int num_kv_heads, int head_dim, int block_size, int num_blocks,
+                           int max_blocks_per_seq, float scale, int dtype, int partition_size, void* workspace,
+                           size_t workspace_bytes, void* stream) {
+    static const char* fn = "paged_attention_decode";
+    int rc;
+    if ((rc = check_pool(fn, num_kv_heads, head_dim, block_size, num_blocks, dtype)) != PKV_OK) return rc;
+    if ((rc = check_heads(fn, num_q_heads, num_kv_heads)) != PKV_OK) return rc;
+    if (num_seqs < 0) return fail(PKV_ERR_INVALID, "%s: num_seqs must be >= 0 (got %d)", fn, num_seqs);
+    if (max_blocks_per_seq <= 0)
+        return fail(PKV_ERR_INVALID, "%s: max_blocks_per_seq must be positive (got %d)", fn, max_blocks_per_seq);
+    if (!std::isfinite(scale) || !(scale > 0.f))
+        return fail(PKV_ERR_INVALID, "%s: scale must be finite and positive", fn);
+    if (partition_size < 0 || (partition_size > 0 && partition_size % block_size != 0))
+        return fail(PKV_ERR_INVALID, "%s: partition_size %d must be 0 or a positive multiple of block_size", fn,
+                    partition_size);
+    const int path = decode_path();
+    if (path < 0) return fail(PKV_ERR_INVALID, "%s: PKV_DECODE_PATH must be auto, valu or mfma", fn);
+    if (path == 2 && dtype == PKV_F32)
+        return fail(PKV_ERR_UNSUPPORTED, "%s: the matrix-core path takes 16-bit types only", fn);
+    if (num_seqs == 0) return PKV_OK;
+    if (!out || !query || !key_cache || !value_cache || !block_tables || !context_lens)
+        return fail(PKV_ERR_INVALID, "%s: null pointer argument", fn);
+    if (!aligned(out, 16) || !aligned(query, 16) || !aligned(key_cache, 16) || !aligned(value_cache, 16) ||
+        !aligned(block_tables, 4) || !aligned(context_lens, 4))
+        return fail(PKV_ERR_INVALID, "%s: misaligned pointer (16 bytes for tensors, 4 for int32 arrays)", fn);
+    const int part = partition_tokens(partition_size);
+    const int mp = max_parts(max_blocks_per_seq, part);
+    const int G = num_q_heads / num_kv_heads;
+    const long long grid = (long long)mp * num_q_heads * num_seqs;  // bound on workgroups of any path
+    if (grid > 0x7fffffffLL) return fail(PKV_ERR_INVALID, "%s: problem too large for one launch", fn);
+    const size_t need = pkv_decode_workspace_size(num_seqs, num_q_heads, num_kv_heads, head_dim, block_size,
+                                                  max_blocks_per_seq, partition_size);
+    if (need > 0 && (!workspace || workspace_bytes < need))
+        return fail(PKV_ERR_WORKSPACE, "%s: workspace of %zu bytes needed, %zu given", fn, need,
+                    workspace ? workspace_bytes : (size_t)0);
+    if (need > 0 && !aligned(workspace, 16)) return fail(PKV_ERR_INVALID, "%s: workspace must be 16-byte aligned", fn);
+
+    pkv::DecodeParams p;
+    p.out = out;
+    p.q = query;
+    p.kc = key_cache;
+    p.vc = value_cache;
+    p.block_tables = block_tables;
+    p.context_lens = context_lens;
+    p.ws_acc = (float*)workspace;
+    p.ws_ml = need > 0 ? (float2*)((char*)workspace + (size_t)num_seqs * num_q_heads * mp * head_dim * sizeof(float))
+                       : nullptr;
+    p.S = num_seqs;
+    p.Hq = num_q_heads;
+    p.Hkv = num_kv_heads;
+    p.G = G;
+    p.D = head_dim;
+    p.NB = num_blocks;
+    p.MB = max_blocks_per_seq;
+    p.part_tokens = part;
+    p.max_parts = mp;
+    p.scale_log2 = scale * pkv::kLog2eHost;
+    hipError_t e = pkv::launch_decode_path(p, dtype, path, (hipStream_t)stream);
+    if (e != hipSuccess) return hip_fail(e, fn);
+    return PKV_OK;
+}
+
+int paged_attention_chunked(void* out, const void* query, const int32_t* cu_q_lens, int num_segs, int total_q,
+                            int max_q_len, const void* key_cache, const void* value_cache,
+                            const int32_t* block_tables, const int32_t* context_lens, int num_q_heads,
+                            int num_kv_heads, int head_dim, int block_size, int num_blocks, int max_blocks_per_seq,
+                            float scale, int dtype, void* stream) {
+    static const char* fn = "paged_attention_chunked";
+    int rc;
+    if ((rc = check_pool(fn, num_kv_heads, head_dim, block_size, num_blocks, dtype)) != PKV_OK) return rc;
+    if ((rc = check_heads(fn, num_q_heads, num_kv_heads)) != PKV_OK) return rc;
+    if (dtype == PKV_F32) return fail(PKV_ERR_UNSUPPORTED, "%s: fp32 is not supported (16-bit types only)", fn);
+    if (num_segs < 0 || total_q < 0 || max_q_len < 0)
+        return fail(PKV_ERR_INVALID, "%s: num_segs, total_q and max_q_len must be >= 0", fn);
+    if (max_blocks_per_seq <= 0)
+        return fail(PKV_ERR_INVALID, "%s: max_blocks_per_seq must be positive (got %d)", fn, max_blocks_per_seq);
+    if (!std::isfinite(scale) || !(scale > 0.f))
+        return fail(PKV_ERR_INVALID, "%s: scale must be finite and positive", fn);
+    if (max_q_len > total_q) return fail(PKV_ERR_INVALID, "%s: max_q_len exceeds total_q", fn);
+    if (num_segs == 0 || total_q == 0 || max_q_len == 0) return PKV_OK;
+    if (!out || !query || !cu_q_lens || !key_cache || !value_cache || !block_tables || !context_lens)
+        return fail(PKV_ERR_INVALID, "%s: null pointer argument", fn);
+    if (!aligned(out, 16) || !aligned(query, 16) || !aligned(key_cache, 16) || !aligned(value_cache, 16) ||
+        !aligned(block_tables, 4) || !aligned(context_lens, 4) || !aligned(cu_q_lens, 4))
+        return fail(PKV_ERR_INVALID, "%s: misaligned pointer", fn);
+    const int G = num_q_heads / num_kv_heads;
+    const long long tiles = ((long long)max_q_len * G + 127) / 128;
+    if (tiles * num_kv_heads * num_segs > 0x7fffffffLL)
+        return fail(PKV_ERR_INVALID, "%s: problem too large for one launch", fn);
+    pkv::ChunkedParams p;
+    p.out = out;
+    p.q = query;
+    p.cu_q_lens = cu_q_lens;
+    p.kc = key_cache;
+    p.vc = value_cache;
+    p.block_tables = block_tables;
+    p.context_lens = context_lens;
+    p.num_segs = num_segs;
+    p.Hq = num_q_heads;
+    p.Hkv = num_kv_heads;
+    p.G = G;
+    p.D = head_dim;
+    p.NB = num_blocks;
+    p.MB = max_blocks_per_seq;
+    p.head_chunk = G;
+    p.max_q_len = max_q_len;
+    p.scale_log2 = scale * pkv::kLog2eHost;
+    hipError_t e = pkv::launch_chunked(p, dtype, (hipStream_t)stream);
+    if (e != hipSuccess) return hip_fail(e, fn);
+    return PKV_OK;
+}
+
+int reshape_and_cache(const void* key, const void* value, void* key_cache, void* value_cache,
+                      const int64_t* slot_mapping, int num_tokens, int num_kv_heads, int head_dim, int block_size,
+                      int num_blocks, int dtype, void* stream) {
+    static const char* fn = "reshape_and_cache";
+    int rc;
+    if ((rc = check_pool(fn, num_kv_heads, head_dim, block_size, num_blocks, dtype)) != PKV_OK) return rc;
+    if (num_tokens < 0) return fail(PKV_ERR_INVALID, "%s: num_tokens must be >= 0 (got %d)", fn, num_tokens);
+    if (num_tokens == 0) return PKV_OK;
+    if (!key || !value || !key_cache || !value_cache || !slot_mapping)
+        return fail(PKV_ERR_INVALID, "%s: null pointer argument", fn);
+    if (!aligned(key, 16) || !aligned(value, 16) || !aligned(key_cache, 16) || !aligned(value_cache, 16) ||
+        !aligned(slot_mapping, 8))
+        return fail(PKV_ERR_INVALID, "%s: misaligned pointer", fn);
+    pkv::CacheParams p;
+    p.key = key;
+    p.value = value;
+    p.kc = key_cache;
+    p.vc = value_cache;
+    p.slots = slot_mapping;
+    p.num_tokens = num_tokens;
+    p.Hkv = num_kv_heads;
+    p.D = head_dim;
+    hipError_t e = pkv::launch_reshape_and_cache(p, dtype, (hipStream_t)stream);
+    if (e != hipSuccess) return hip_fail(e, fn);
+    return PKV_OK;
+}
+
+int copy_blocks(void* const* key_caches, void* const* value_caches, int num_layers, const int64_t* block_mapping,
+                int num_pairs, int num_kv_heads, int head_dim, int block_size, int num_blocks, int dtype,
+                void* stream) {
+    static const char* fn = "copy_blocks";
+    int rc;
+    if ((rc = check_pool(fn, num_kv_heads, head_dim, block_size, num_blocks, dtype)) != PKV_OK) return rc;
+    if (num_layers < 0 || num_pairs < 0)
+        return fail(PKV_ERR_INVALID, "%s: num_layers and num_pairs must be >= 0", fn);
+    if (num_layers == 0 || num_pairs == 0) return PKV_OK;
+    if (!key_caches || !value_caches || !block_mapping) return fail(PKV_ERR_INVALID, "%s: null pointer argument", fn);
+    if (!aligned(block_mapping, 8)) return fail(PKV_ERR_INVALID, "%s: misaligned block_mapping", fn);
+    for (int l = 0; l < num_layers; ++l) {
+        if (!key_caches[l] || !value_caches[l])
+            return fail(PKV_ERR_INVALID, "%s: null cache pointer for layer %d", fn, l);
+        if (!aligned(key_caches[l], 16) || !aligned(value_caches[l], 16))
+            return fail(PKV_ERR_INVALID, "%s: misaligned cache pointer for layer %d", fn, l);
+    }
+    const int esz = dtype == PKV_F32 ? 4 : 2;
+    pkv::CopyParams p;
+    p.mapping = block_mapping;
+    p.num_pairs = num_pairs;
+    p.block_bytes = (size_t)num_kv_heads * block_size * head_dim * esz;
+    for (int l0 = 0; l0 < num_layers; l0 += pkv::kMaxLayersPerLaunch) {
+        const int nl = num_layers - l0 < pkv::kMaxLayersPerLaunch ? num_layers - l0 : pkv::kMaxLayersPerLaunch;
+        for (int i = 0; i < nl; ++i) {
+            p.k[i] = key_caches[l0 + i];
+            p.v[i] = value_caches[l0 + i];
+        }
+        hipError_t e = pkv::launch_copy_blocks(p, nl, (hipStream_t)stream);
+        if (e != hipSuccess) return hip_fail(e, fn);
+    }
+    return PKV_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,104 @@
+// device.h -- element types, conversions and CDNA4 matrix-core wrappers shared by
+// the gfx950 kernels of this library.  Device code only.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace pkv {
+
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+typedef _Float16 f16x4 __attribute__((ext_vector_type(4)));
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+
+// Element kinds.  Storage is always raw bits; arithmetic is fp32.
+enum Kind { KF32 = 0, KF16 = 1, KBF16 = 2 };
+
+template <int K> struct Elem;
+template <> struct Elem<KF32> { typedef float bits; static constexpr int bytes = 4; };
+template <> struct Elem<KF16> { typedef uint16_t bits; static constexpr int bytes = 2; };
+template <> struct Elem<KBF16> { typedef uint16_t bits; static constexpr int bytes = 2; };
+
+// ---- conversions -------------------------------------------------------------------
+
+// low / high 16-bit half of a 32-bit word, widened to fp32
+template <int K> __device__ __forceinline__ float lo16(uint32_t w);
+template <int K> __device__ __forceinline__ float hi16(uint32_t w);
+template <> __device__ __forceinline__ float lo16<KBF16>(uint32_t w) { return __uint_as_float(w << 16); }
+template <> __device__ __forceinline__ float hi16<KBF16>(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
+template <> __device__ __forceinline__ float lo16<KF16>(uint32_t w) {
+    return (float)__builtin_bit_cast(f16x2, w)[0];
+}
+template <> __device__ __forceinline__ float hi16<KF16>(uint32_t w) {
+    return (float)__builtin_bit_cast(f16x2, w)[1];
+}
+
+// fp32 -> storage bits, round to nearest even (hardware conversions on gfx950)
+template <int K> __device__ __forceinline__ uint16_t to_bits16(float x);
+template <> __device__ __forceinline__ uint16_t to_bits16<KBF16>(float x) {
+    return __builtin_bit_cast(uint16_t, (__bf16)x);
+}
+template <> __device__ __forceinline__ uint16_t to_bits16<KF16>(float x) {
+    return __builtin_bit_cast(uint16_t, (_Float16)x);
+}
+
+template <int K> __device__ __forceinline__ void store_elem(void* base, size_t i, float x) {
+    if constexpr (K == KF32)
+        ((float*)base)[i] = x;
+    else
+        ((uint16_t*)base)[i] = to_bits16<K>(x);
+}
+
+// Four fp32 values -> four 16-bit values packed in 8 bytes.
+template <int K> __device__ __forceinline__ uint2 pack4(float a, float b, float c, float d) {
+    uint2 r;
+    r.x = (uint32_t)to_bits16<K>(a) | ((uint32_t)to_bits16<K>(b) << 16);
+    r.y = (uint32_t)to_bits16<K>(c) | ((uint32_t)to_bits16<K>(d) << 16);
+    return r;
+}
+
+// ---- matrix cores --------------------------------------------------------------------
+// 16x16x32 (A: 16 rows x 32 k, 8 elements per lane; lane l holds row l%16,
+// k = 8*(l/16)..+7; B symmetric with columns) and 16x16x16 (4 elements per lane,
+// k = 4*(l/16)..+3).  Result: lane l holds rows 4*(l/16)..+3 of column l%16.
+template <int K> __device__ __forceinline__ f32x4 mma_16x16x32(uint4 a, uint4 b, f32x4 c);
+template <> __device__ __forceinline__ f32x4 mma_16x16x32<KBF16>(uint4 a, uint4 b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a), __builtin_bit_cast(bf16x8, b), c,
+                                                   0, 0, 0);
+}
+template <> __device__ __forceinline__ f32x4 mma_16x16x32<KF16>(uint4 a, uint4 b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8, a), __builtin_bit_cast(f16x8, b), c, 0,
+                                                  0, 0);
+}
+template <int K> __device__ __forceinline__ f32x4 mma_16x16x16(uint2 a, uint2 b, f32x4 c);
+template <> __device__ __forceinline__ f32x4 mma_16x16x16<KBF16>(uint2 a, uint2 b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(i16x4, a), __builtin_bit_cast(i16x4, b), c,
+                                                     0, 0, 0);
+}
+template <> __device__ __forceinline__ f32x4 mma_16x16x16<KF16>(uint2 a, uint2 b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x16f16(__builtin_bit_cast(f16x4, a), __builtin_bit_cast(f16x4, b), c, 0,
+                                                 0, 0);
+}
+
+// ---- misc ------------------------------------------------------------------------------
+
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+__device__ __forceinline__ int lane_id() { return (int)(threadIdx.x & 63); }
+
+// value of a wave-uniform register from lane `src` (src must be wave-uniform)
+__device__ __forceinline__ int read_lane(int v, int src) { return __builtin_amdgcn_readlane(v, src); }
+__device__ __forceinline__ float read_lane(float v, int src) {
+    return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), src));
+}
+
+__device__ __forceinline__ float xor_max(float v, int mask) { return fmaxf(v, __shfl_xor(v, mask, 64)); }
+__device__ __forceinline__ float xor_sum(float v, int mask) { return v + __shfl_xor(v, mask, 64); }
+
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kNegInf = -__builtin_huge_valf();
+
+}  // namespace pkv

@@ -1,0 +1,69 @@
+// internal.h -- parameter blocks passed by value to the kernels, and the launchers
+// that api.cpp calls after validating the public arguments.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace pkv {
+
+constexpr int kBlockSize = 16;  // tokens per KV block (the only block size compiled)
+constexpr float kLog2eHost = 1.4426950408889634f;
+
+struct DecodeParams {
+    void* out;
+    const void* q;
+    const void* kc;
+    const void* vc;
+    const int32_t* block_tables;
+    const int32_t* context_lens;
+    float* ws_acc;   // [S][Hq][max_parts][D] unnormalised partial outputs
+    float2* ws_ml;   // [S][Hq][max_parts] (running max in log2 units, running sum)
+    int S, Hq, Hkv, G, D, NB, MB;
+    int part_tokens;  // tokens per partition, multiple of kBlockSize
+    int max_parts;    // ceil(MB * kBlockSize / part_tokens)
+    float scale_log2; // scale * log2(e): scores are kept in log2 units
+};
+
+struct ChunkedParams {
+    void* out;
+    const void* q;
+    const int32_t* cu_q_lens;
+    const void* kc;
+    const void* vc;
+    const int32_t* block_tables;
+    const int32_t* context_lens;
+    int num_segs, Hq, Hkv, G, D, NB, MB;
+    int head_chunk;   // query heads of one group handled together (<= G)
+    int max_q_len;
+    float scale_log2;
+};
+
+struct CacheParams {
+    const void* key;
+    const void* value;
+    void* kc;
+    void* vc;
+    const int64_t* slots;
+    int num_tokens, Hkv, D;
+};
+
+constexpr int kMaxLayersPerLaunch = 32;
+struct CopyParams {
+    void* k[kMaxLayersPerLaunch];
+    void* v[kMaxLayersPerLaunch];
+    const int64_t* mapping;
+    int num_pairs;
+    size_t block_bytes;  // bytes of one block of K (same for V)
+};
+
+// kind: 0 f32, 1 f16, 2 bf16
+hipError_t launch_decode(const DecodeParams& p, int kind, hipStream_t stream);
+// path: 0 automatic, 1 vector ALU inner loop, 2 matrix-core inner loop (16-bit types)
+hipError_t launch_decode_path(const DecodeParams& p, int kind, int path, hipStream_t stream);
+hipError_t launch_chunked(const ChunkedParams& p, int kind, hipStream_t stream);
+hipError_t launch_reshape_and_cache(const CacheParams& p, int kind, hipStream_t stream);
+hipError_t launch_copy_blocks(const CopyParams& p, int num_layers, hipStream_t stream);
+
+}  // namespace pkv
