@@ -53,13 +53,26 @@ int check_heads(const char* fn, int num_q_heads, int num_kv_heads) {
     return PKV_OK;
 }
 
-constexpr int kAutoPartition = 512;
-
-int partition_tokens(int partition_size) { return partition_size > 0 ? partition_size : kAutoPartition; }
-
 int max_parts(int max_blocks_per_seq, int part) {
     const long long tokens = (long long)max_blocks_per_seq * pkv::kBlockSize;
     return (int)((tokens + part - 1) / part);
+}
+
+// Largest (query-head chunks x record capacity) over the inner loops a decode
+// with G heads per kv head may use, and the largest record capacity.
+void record_shape(int G, long long* heads_per_kv, int* cap_max) {
+    const int ht_mfma = G <= 16 ? 16 : 32;
+    const int ht_valu = G == 1 ? 1 : (G == 2 ? 2 : 4);
+    long long best = 0;
+    int cap = 0;
+    for (int ht : {ht_mfma, ht_valu}) {
+        const int c = G < ht ? G : ht;
+        const long long chunks = (G + ht - 1) / ht;
+        if (chunks * c > best) best = chunks * c;
+        if (c > cap) cap = c;
+    }
+    *heads_per_kv = best;
+    *cap_max = cap;
 }
 
 // Decode path override for testing and measurement: PKV_DECODE_PATH=valu|mfma.
@@ -99,17 +112,24 @@ int pkv_decode_partition_size(int num_seqs, int num_q_heads, int num_kv_heads, i
     (void)max_blocks_per_seq;
     if (block_size <= 0) return PKV_ERR_INVALID;
     if (partition_size < 0 || (partition_size > 0 && partition_size % block_size != 0)) return PKV_ERR_INVALID;
-    return partition_tokens(partition_size);
+    return partition_size;  // 0: balanced split sized at launch
 }
 
 size_t pkv_decode_workspace_size(int num_seqs, int num_q_heads, int num_kv_heads, int head_dim, int block_size,
                                  int max_blocks_per_seq, int partition_size) {
-    const int part = pkv_decode_partition_size(num_seqs, num_q_heads, num_kv_heads, head_dim, block_size,
-                                               max_blocks_per_seq, partition_size);
-    if (part <= 0 || num_seqs <= 0 || num_q_heads <= 0 || head_dim <= 0 || max_blocks_per_seq <= 0) return 0;
-    const int mp = max_parts(max_blocks_per_seq, part);
+    if (num_seqs <= 0 || num_q_heads <= 0 || num_kv_heads <= 0 || num_q_heads % num_kv_heads != 0 ||
+        head_dim <= 0 || block_size <= 0 || max_blocks_per_seq <= 0 || partition_size < 0 ||
+        (partition_size > 0 && partition_size % block_size != 0))
+        return 0;
+    const int G = num_q_heads / num_kv_heads;
+    long long heads_per_kv = 0;
+    int cap = 0;
+    record_shape(G, &heads_per_kv, &cap);
+    const size_t per_head = ((size_t)head_dim + 2) * sizeof(float);
+    if (partition_size == 0) return (size_t)pkv::kMaxSplitWaves * 2 * cap * per_head;
+    const int mp = max_parts(max_blocks_per_seq, partition_size);
     if (mp <= 1) return 0;
-    return (size_t)num_seqs * num_q_heads * mp * ((size_t)head_dim * sizeof(float) + sizeof(float2));
+    return (size_t)num_seqs * num_kv_heads * heads_per_kv * mp * per_head;
 }
 
 int paged_attention_decode(void* out, const void* query, const void* key_cache, const void* value_cache,
@@ -139,10 +159,9 @@ int paged_attention_decode(void* out, const void* query, const void* key_cache, 
     if (!aligned(out, 16) || !aligned(query, 16) || !aligned(key_cache, 16) || !aligned(value_cache, 16) ||
         !aligned(block_tables, 4) || !aligned(context_lens, 4))
         return fail(PKV_ERR_INVALID, "%s: misaligned pointer (16 bytes for tensors, 4 for int32 arrays)", fn);
-    const int part = partition_tokens(partition_size);
-    const int mp = max_parts(max_blocks_per_seq, part);
+    const int mp = partition_size > 0 ? max_parts(max_blocks_per_seq, partition_size) : 0;
     const int G = num_q_heads / num_kv_heads;
-    const long long grid = (long long)mp * num_q_heads * num_seqs;  // bound on workgroups of any path
+    const long long grid = (long long)(mp > 0 ? mp : 1) * num_q_heads * num_seqs;  // bound on workgroups
     if (grid > 0x7fffffffLL) return fail(PKV_ERR_INVALID, "%s: problem too large for one launch", fn);
     const size_t need = pkv_decode_workspace_size(num_seqs, num_q_heads, num_kv_heads, head_dim, block_size,
                                                   max_blocks_per_seq, partition_size);
@@ -158,9 +177,7 @@ int paged_attention_decode(void* out, const void* query, const void* key_cache, 
     p.vc = value_cache;
     p.block_tables = block_tables;
     p.context_lens = context_lens;
-    p.ws_acc = (float*)workspace;
-    p.ws_ml = need > 0 ? (float2*)((char*)workspace + (size_t)num_seqs * num_q_heads * mp * head_dim * sizeof(float))
-                       : nullptr;
+    p.ws = (float*)workspace;
     p.S = num_seqs;
     p.Hq = num_q_heads;
     p.Hkv = num_kv_heads;
@@ -168,7 +185,8 @@ int paged_attention_decode(void* out, const void* query, const void* key_cache, 
     p.D = head_dim;
     p.NB = num_blocks;
     p.MB = max_blocks_per_seq;
-    p.part_tokens = part;
+    p.chunks = 1;
+    p.part_tokens = partition_size;
     p.max_parts = mp;
     p.scale_log2 = scale * pkv::kLog2eHost;
     hipError_t e = pkv::launch_decode_path(p, dtype, path, (hipStream_t)stream);

@@ -1,0 +1,322 @@
+// decode_inner.h -- the two per-block inner loops of paged decode (gfx950), shared
+// by the fixed-partition and the load-balanced kernels.
+//
+// One wave owns one (sequence, kv head, query-head tile) stream at a time and
+// folds 16-token blocks into an online softmax: running max m and running sum l
+// per query head (scores in log2 units), accumulator rescaled by 2^(m_old - m_new).
+// Tokens at or past the context end are masked; their V slots may hold anything
+// (NaN), so those V values are zeroed before the P.V product.
+#pragma once
+
+#include "device.h"
+#include "internal.h"
+
+namespace pkv {
+
+// ---------------------------------------------------------------------------------------
+// Matrix-core inner loop (16-bit types).  Scores S^T[16 tokens][16 heads] = K Q^T on
+// 16x16x32 MFMA (lane l: token row l%16 of K, head column l%16 of Q, d-chunk
+// (l/16 + 4*step) -- the same head_dim permutation on both operands).  The result
+// leaves lane l with 4 tokens (4*(l/16)+j) of head l%16, exactly the B operand of
+// O^T[d][head] += V^T[d][16 tokens] P^T[16 tokens][head] on 16x16x16 MFMA, whose
+// A operand is 8 contiguous bytes of the head_dim-major V tile.  P is split into a
+// 16-bit high part and a 16-bit remainder, so the product keeps ~16 bits of P.
+// ---------------------------------------------------------------------------------------
+template <int K, int D, int NH>
+struct MfmaLoop {
+    static constexpr int KS = D / 32;
+    static constexpr int DT = D / 16;
+    static constexpr int HT = 16 * NH;
+    // waves per SIMD the register budget is sized for (two 16-head tiles need more)
+    static constexpr int kWaves = NH == 1 ? 2 : 1;
+
+    struct Tile {
+        uint4 k[KS];
+        uint2 v[DT];
+    };
+    struct State {
+        float m[NH], l[NH];
+        f32x4 acc[NH][DT];
+        uint4 q[NH][KS];
+    };
+
+    int col, gq;
+    uint32_t koff, voff;  // byte offsets of this lane's first K / V piece inside a tile
+
+    __device__ __forceinline__ void init_lane(int lane) {
+        col = lane & 15;
+        gq = lane >> 4;
+        koff = (uint32_t)(col * D + gq * 8) * 2;                // + ks * 64 bytes
+        voff = (uint32_t)(col * kBlockSize + 4 * gq) * 2;        // + dt * 512 bytes
+    }
+
+    // query rows head0 .. head0 + nh - 1 of token row `qrow` (q is [rows][Hq][D])
+    __device__ __forceinline__ void start(State& st, const void* q, size_t qrow, int Hq, int head0, int nh) {
+        const uint16_t* qp = (const uint16_t*)q;
+#pragma unroll
+        for (int ht = 0; ht < NH; ++ht) {
+            const int h = ht * 16 + col;
+#pragma unroll
+            for (int ks = 0; ks < KS; ++ks)
+                st.q[ht][ks] = h < nh ? *(const uint4*)(qp + (qrow * Hq + head0 + h) * D + (gq + 4 * ks) * 8)
+                                      : make_uint4(0, 0, 0, 0);
+            st.m[ht] = kNegInf;
+            st.l[ht] = 0.f;
+#pragma unroll
+            for (int dt = 0; dt < DT; ++dt) st.acc[ht][dt] = f32x4{0.f, 0.f, 0.f, 0.f};
+        }
+    }
+
+    __device__ __forceinline__ void load(Tile& t, const void* kc, const void* vc, size_t tile_index) const {
+        const char* kt = (const char*)kc + tile_index * (kBlockSize * D * 2) + koff;
+        const char* vt = (const char*)vc + tile_index * (kBlockSize * D * 2) + voff;
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) t.k[ks] = *(const uint4*)(kt + ks * 64);
+#pragma unroll
+        for (int dt = 0; dt < DT; ++dt) t.v[dt] = *(const uint2*)(vt + dt * 512);
+    }
+
+    // fold one block whose first `valid` tokens are inside the context
+    __device__ __forceinline__ void block(State& st, Tile& t, int valid, float scale_log2) const {
+        uint2 phi[NH], plo[NH];
+#pragma unroll
+        for (int ht = 0; ht < NH; ++ht) {
+            f32x4 sc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int ks = 0; ks < KS; ++ks) sc = mma_16x16x32<K>(t.k[ks], st.q[ht][ks], sc);
+            float sv[4];
+#pragma unroll
+            for (int j = 0; j < 4; ++j) sv[j] = (4 * gq + j < valid) ? sc[j] * scale_log2 : kNegInf;
+            float bm = fmaxf(fmaxf(sv[0], sv[1]), fmaxf(sv[2], sv[3]));
+            bm = xor_max(bm, 16);
+            bm = xor_max(bm, 32);
+            const float mn = fmaxf(st.m[ht], bm);
+            const float alpha = fast_exp2(st.m[ht] - mn);
+            float pr[4];
+#pragma unroll
+            for (int j = 0; j < 4; ++j) pr[j] = fast_exp2(sv[j] - mn);
+            st.l[ht] = st.l[ht] * alpha + ((pr[0] + pr[1]) + (pr[2] + pr[3]));
+            st.m[ht] = mn;
+#pragma unroll
+            for (int dt = 0; dt < DT; ++dt) st.acc[ht][dt] *= alpha;
+            phi[ht] = pack4<K>(pr[0], pr[1], pr[2], pr[3]);
+            plo[ht] = pack4<K>(pr[0] - lo16<K>(phi[ht].x), pr[1] - hi16<K>(phi[ht].x), pr[2] - lo16<K>(phi[ht].y),
+                               pr[3] - hi16<K>(phi[ht].y));
+        }
+        if (valid < kBlockSize) {
+            const int tk = 4 * gq;
+#pragma unroll
+            for (int dt = 0; dt < DT; ++dt) {
+                uint32_t x = t.v[dt].x, y = t.v[dt].y;
+                if (tk + 0 >= valid) x &= 0xffff0000u;
+                if (tk + 1 >= valid) x &= 0x0000ffffu;
+                if (tk + 2 >= valid) y &= 0xffff0000u;
+                if (tk + 3 >= valid) y &= 0x0000ffffu;
+                t.v[dt] = make_uint2(x, y);
+            }
+        }
+        // high parts first, then the remainders: consecutive MFMAs never share an accumulator
+#pragma unroll
+        for (int ht = 0; ht < NH; ++ht)
+#pragma unroll
+            for (int dt = 0; dt < DT; ++dt) st.acc[ht][dt] = mma_16x16x16<K>(t.v[dt], phi[ht], st.acc[ht][dt]);
+#pragma unroll
+        for (int ht = 0; ht < NH; ++ht)
+#pragma unroll
+            for (int dt = 0; dt < DT; ++dt) st.acc[ht][dt] = mma_16x16x16<K>(t.v[dt], plo[ht], st.acc[ht][dt]);
+    }
+
+    // sum l over the four lane groups (each holds a quarter of the tokens)
+    __device__ __forceinline__ void finish(State& st) const {
+#pragma unroll
+        for (int ht = 0; ht < NH; ++ht) st.l[ht] = xor_sum(xor_sum(st.l[ht], 16), 32);
+    }
+
+    // normalised output of heads head0 .. head0 + nh - 1 of token row `orow`
+    __device__ __forceinline__ void store_out(const State& st, void* out, size_t orow, int Hq, int head0,
+                                              int nh) const {
+#pragma unroll
+        for (int ht = 0; ht < NH; ++ht) {
+            const int h = ht * 16 + col;
+            if (h >= nh) continue;
+            const float inv = st.l[ht] > 0.f ? 1.f / st.l[ht] : 0.f;
+            uint16_t* o = (uint16_t*)out + (orow * Hq + head0 + h) * D;
+#pragma unroll
+            for (int dt = 0; dt < DT; ++dt) {
+                const f32x4 a = st.acc[ht][dt];
+                *(uint2*)(o + dt * 16 + 4 * gq) = pack4<K>(a[0] * inv, a[1] * inv, a[2] * inv, a[3] * inv);
+            }
+        }
+    }
+
+    // partial record: acc[cap][D], m[cap], l[cap] (cap = head capacity of a record)
+    __device__ __forceinline__ void store_partial(const State& st, float* rec, int cap, int nh) const {
+#pragma unroll
+        for (int ht = 0; ht < NH; ++ht) {
+            const int h = ht * 16 + col;
+            if (h >= nh) continue;
+#pragma unroll
+            for (int dt = 0; dt < DT; ++dt) *(f32x4*)(rec + h * D + dt * 16 + 4 * gq) = st.acc[ht][dt];
+            if (gq == 0) {
+                rec[cap * D + h] = st.m[ht];
+                rec[cap * D + cap + h] = st.l[ht];
+            }
+        }
+    }
+};
+
+// ---------------------------------------------------------------------------------------
+// Vector-ALU inner loop (fp32, or few query heads per kv head).  Four lanes per
+// token share its dot products (shuffle reductions); for P.V each lane owns
+// D/64 head_dim rows of the head_dim-major V tile and all 16 tokens of them.
+// ---------------------------------------------------------------------------------------
+template <int K> __device__ __forceinline__ void widen16(uint4 c, float* f) {
+    if constexpr (K == KF32) {
+        f[0] = __uint_as_float(c.x);
+        f[1] = __uint_as_float(c.y);
+        f[2] = __uint_as_float(c.z);
+        f[3] = __uint_as_float(c.w);
+    } else {
+        const uint32_t u[4] = {c.x, c.y, c.z, c.w};
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            f[2 * i] = lo16<K>(u[i]);
+            f[2 * i + 1] = hi16<K>(u[i]);
+        }
+    }
+}
+
+template <int K, int D, int GT>
+struct ValuLoop {
+    static constexpr int EB = Elem<K>::bytes;
+    static constexpr int VE = 16 / EB;                 // elements per 16-byte chunk
+    static constexpr int KC = D / VE / 4;              // K chunks per lane
+    static constexpr int DR = D / 64;                  // output rows per lane
+    static constexpr int VC = DR * kBlockSize * EB / 16;  // V chunks per lane
+    static constexpr int HT = GT;
+    static constexpr int kWaves = (D == 128 && (EB == 4 || GT == 4)) ? 1 : 2;
+
+    struct Tile {
+        uint4 k[KC];
+        uint4 v[VC];
+    };
+    struct State {
+        float m[GT], l[GT], acc[GT][DR];
+        float q[GT][KC * VE];
+    };
+
+    int lane, tq, sub;
+
+    __device__ __forceinline__ void init_lane(int ln) {
+        lane = ln;
+        tq = ln >> 2;
+        sub = ln & 3;
+    }
+
+    __device__ __forceinline__ void start(State& st, const void* q, size_t qrow, int Hq, int head0, int nh) {
+        const char* qp = (const char*)q;
+#pragma unroll
+        for (int j = 0; j < GT; ++j) {
+#pragma unroll
+            for (int k = 0; k < KC; ++k) {
+                uint4 c = make_uint4(0, 0, 0, 0);
+                if (j < nh) c = *(const uint4*)(qp + ((qrow * Hq + head0 + j) * D + (sub + 4 * k) * VE) * EB);
+                widen16<K>(c, &st.q[j][k * VE]);
+            }
+            st.m[j] = kNegInf;
+            st.l[j] = 0.f;
+#pragma unroll
+            for (int r = 0; r < DR; ++r) st.acc[j][r] = 0.f;
+        }
+    }
+
+    __device__ __forceinline__ void load(Tile& t, const void* kc, const void* vc, size_t tile_index) const {
+        const size_t base = tile_index * (size_t)(kBlockSize * D * EB);
+        const char* kt = (const char*)kc + base + (size_t)tq * D * EB;
+        const char* vt = (const char*)vc + base + (size_t)lane * DR * kBlockSize * EB;
+#pragma unroll
+        for (int k = 0; k < KC; ++k) t.k[k] = *(const uint4*)(kt + (sub + 4 * k) * 16);
+#pragma unroll
+        for (int c = 0; c < VC; ++c) t.v[c] = *(const uint4*)(vt + c * 16);
+    }
+
+    __device__ __forceinline__ void block(State& st, Tile& t, int valid, float scale_log2) const {
+        float kf[KC * VE];
+#pragma unroll
+        for (int k = 0; k < KC; ++k) widen16<K>(t.k[k], &kf[k * VE]);
+        float pj[GT];
+#pragma unroll
+        for (int j = 0; j < GT; ++j) {
+            float dot = 0.f;
+#pragma unroll
+            for (int i = 0; i < KC * VE; ++i) dot = fmaf(st.q[j][i], kf[i], dot);
+            dot = xor_sum(dot, 1);
+            dot = xor_sum(dot, 2);
+            const float sv = tq < valid ? dot * scale_log2 : kNegInf;
+            float bm = xor_max(sv, 4);
+            bm = xor_max(bm, 8);
+            bm = xor_max(bm, 16);
+            bm = xor_max(bm, 32);
+            const float mn = fmaxf(st.m[j], bm);
+            const float alpha = fast_exp2(st.m[j] - mn);
+            pj[j] = fast_exp2(sv - mn);
+            st.l[j] = st.l[j] * alpha + (sub == 0 ? pj[j] : 0.f);
+            st.m[j] = mn;
+#pragma unroll
+            for (int r = 0; r < DR; ++r) st.acc[j][r] *= alpha;
+        }
+        float vf[DR * kBlockSize];  // vf[r * 16 + token]
+#pragma unroll
+        for (int c = 0; c < VC; ++c) widen16<K>(t.v[c], &vf[c * VE]);
+        if (valid < kBlockSize) {
+#pragma unroll
+            for (int r = 0; r < DR; ++r)
+#pragma unroll
+                for (int tk = 0; tk < kBlockSize; ++tk)
+                    if (tk >= valid) vf[r * kBlockSize + tk] = 0.f;
+        }
+#pragma unroll
+        for (int j = 0; j < GT; ++j) {
+#pragma unroll
+            for (int tk = 0; tk < kBlockSize; ++tk) {
+                const float pt = read_lane(pj[j], 4 * tk);
+#pragma unroll
+                for (int r = 0; r < DR; ++r) st.acc[j][r] = fmaf(pt, vf[r * kBlockSize + tk], st.acc[j][r]);
+            }
+        }
+    }
+
+    __device__ __forceinline__ void finish(State& st) const {
+#pragma unroll
+        for (int j = 0; j < GT; ++j)
+#pragma unroll
+            for (int mask = 1; mask < 64; mask <<= 1) st.l[j] = xor_sum(st.l[j], mask);
+    }
+
+    __device__ __forceinline__ void store_out(const State& st, void* out, size_t orow, int Hq, int head0,
+                                              int nh) const {
+#pragma unroll
+        for (int j = 0; j < GT; ++j) {
+            if (j >= nh) continue;
+            const float inv = st.l[j] > 0.f ? 1.f / st.l[j] : 0.f;
+#pragma unroll
+            for (int r = 0; r < DR; ++r)
+                store_elem<K>(out, (orow * Hq + head0 + j) * D + lane * DR + r, st.acc[j][r] * inv);
+        }
+    }
+
+    __device__ __forceinline__ void store_partial(const State& st, float* rec, int cap, int nh) const {
+#pragma unroll
+        for (int j = 0; j < GT; ++j) {
+            if (j >= nh) continue;
+#pragma unroll
+            for (int r = 0; r < DR; ++r) rec[j * D + lane * DR + r] = st.acc[j][r];
+            if (lane == 0) {
+                rec[cap * D + j] = st.m[j];
+                rec[cap * D + cap + j] = st.l[j];
+            }
+        }
+    }
+};
+
+}  // namespace pkv

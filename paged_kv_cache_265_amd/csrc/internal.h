@@ -18,13 +18,16 @@ struct DecodeParams {
     const void* vc;
     const int32_t* block_tables;
     const int32_t* context_lens;
-    float* ws_acc;   // [S][Hq][max_parts][D] unnormalised partial outputs
-    float2* ws_ml;   // [S][Hq][max_parts] (running max in log2 units, running sum)
+    float* ws;        // partial records: acc[cap][D], m[cap], l[cap] (m in log2 units)
     int S, Hq, Hkv, G, D, NB, MB;
-    int part_tokens;  // tokens per partition, multiple of kBlockSize
-    int max_parts;    // ceil(MB * kBlockSize / part_tokens)
+    int chunks;       // query-head chunks per kv head (set by the launcher)
+    int part_tokens;  // 0: balanced split; else tokens per fixed partition (multiple of kBlockSize)
+    int max_parts;    // fixed partitions: ceil(MB * kBlockSize / part_tokens)
     float scale_log2; // scale * log2(e): scores are kept in log2 units
 };
+
+// upper bound on the one-wave workgroups of the balanced split (sizes its workspace)
+constexpr int kMaxSplitWaves = 8192;
 
 struct ChunkedParams {
     void* out;

@@ -8,12 +8,28 @@ import torch
 
 import oracle
 
-# acceptance bar: fp32 inputs max abs error <= 1e-5; 16-bit inputs max abs error
-# <= 2e-3 and, per output row (one query head of one token), max |err| / max |ref|
-# <= 1e-2 (a relative error per element is not used as a gate: outputs cross zero)
+# Acceptance bar.  fp32 inputs: max abs error <= 1e-5.  16-bit inputs: the
+# (atol, rtol) = (2e-3, 1e-2) pair applied per element as |err| <= atol + rtol*|ref|
+# (a bf16 output above 0.5 in magnitude cannot be stored within 2e-3 of the exact
+# value: half a bf16 ulp is 2^-9 |o|), and per output row (one query head of one
+# token) max |err| / max |ref| <= 1e-2.
 TOL_F32_ABS = 1e-5
 TOL_16_ABS = 2e-3
+TOL_16_REL = 1e-2
 TOL_16_ROW_REL = 1e-2
+# Tighter check of the arithmetic: outputs are the fp32 result rounded to the
+# 16-bit type, so they may sit at most half an ulp of that type (plus the fp32
+# accumulation error) from the exact value.
+ULP_SLACK = 0.5
+FP32_REL = 3e-5
+
+
+def ulp16(ref: np.ndarray, dtype: str) -> np.ndarray:
+    """Spacing of the 16-bit type at |ref| (normal range; subnormal floor)."""
+    mant = 7 if dtype == "bf16" else 10
+    floor = 2.0 ** -133 if dtype == "bf16" else 2.0 ** -24
+    e = np.floor(np.log2(np.maximum(np.abs(ref), 1e-300)))
+    return np.maximum(2.0 ** (e - mant), floor)
 
 
 def dev(x, device="cuda"):
@@ -23,7 +39,7 @@ def dev(x, device="cuda"):
 
 
 def check_close(gpu: torch.Tensor, ref: np.ndarray, dtype: str, what: str = "") -> dict:
-    """Assert the acceptance bar; returns the error statistics."""
+    """Assert the acceptance bar and the half-ulp check; returns error statistics."""
     g = gpu.detach().to("cpu").to(torch.float64).numpy().reshape(ref.shape)
     assert np.isfinite(g).all(), f"{what}: non-finite output"
     err = np.abs(g - ref)
@@ -31,14 +47,21 @@ def check_close(gpu: torch.Tensor, ref: np.ndarray, dtype: str, what: str = "") 
     if dtype == "f32":
         assert stats["max_abs"] <= TOL_F32_ABS, f"{what}: max abs err {stats['max_abs']:.3e}"
         return stats
+    bound = TOL_16_ABS + TOL_16_REL * np.abs(ref)
+    worst = float((err / bound).max()) if err.size else 0.0
+    stats["tol_used"] = worst
     rows_ref = np.abs(ref).reshape(-1, ref.shape[-1]).max(axis=1)
     rows_err = err.reshape(-1, ref.shape[-1]).max(axis=1)
     live = rows_ref > 0
     rel = rows_err[live] / rows_ref[live]
     stats["max_row_rel"] = float(rel.max()) if rel.size else 0.0
-    assert stats["max_abs"] <= TOL_16_ABS, f"{what}: max abs err {stats['max_abs']:.3e}"
+    rowmax = np.repeat(rows_ref, ref.shape[-1]).reshape(ref.shape)
+    ulps = err / (ulp16(ref, dtype) * ULP_SLACK + FP32_REL * rowmax + 1e-30)
+    stats["ulp_check"] = float(ulps.max()) if ulps.size else 0.0
+    assert worst <= 1.0, f"{what}: error beyond atol+rtol*|ref| by factor {worst:.3f} (max abs {stats['max_abs']:.3e})"
     assert stats["max_row_rel"] <= TOL_16_ROW_REL, f"{what}: max row rel err {stats['max_row_rel']:.3e}"
     assert np.all(rows_err[~live] == 0), f"{what}: zero reference rows must give exact zeros"
+    assert stats["ulp_check"] <= 1.0, f"{what}: beyond half an ulp plus fp32 error (x{stats['ulp_check']:.2f})"
     return stats
 
 

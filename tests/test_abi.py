@@ -50,13 +50,18 @@ def test_status_strings():
 
 
 def test_workspace_size_matches_layout():
-    # partitions of 512 tokens: 512 blocks x 16 = 8192 tokens -> 16 partitions
-    assert pkv.decode_partition_size(256, 32, 8, 128, 16, 512) == 512
-    assert pkv.decode_workspace_size(256, 32, 8, 128, 16, 512) == 256 * 32 * 16 * (128 * 4 + 8)
-    # one partition covers everything: no workspace
-    assert pkv.decode_workspace_size(4, 4, 4, 64, 16, 3) == 0
+    rec = lambda cap, D: cap * (D + 2) * 4  # noqa: E731  acc[cap][D] + m[cap] + l[cap], fp32
+    # balanced split (partition_size 0): two records per wave for at most 8192 waves
+    assert pkv.decode_partition_size(256, 32, 8, 128, 16, 512) == 0
+    assert pkv.decode_workspace_size(256, 32, 8, 128, 16, 512) == 8192 * 2 * rec(4, 128)
+    assert pkv.decode_workspace_size(32, 32, 1, 128, 16, 8192) == 8192 * 2 * rec(32, 128)
+    assert pkv.decode_workspace_size(4, 4, 4, 64, 16, 3) == 8192 * 2 * rec(1, 64)
+    # fixed partitions: one record per (sequence, kv head, partition); none when one partition fits all
     assert pkv.decode_workspace_size(8, 8, 8, 64, 16, 32, partition_size=512) == 0
-    assert pkv.decode_workspace_size(8, 8, 8, 64, 16, 33, partition_size=512) == 8 * 8 * 2 * (64 * 4 + 8)
+    assert pkv.decode_workspace_size(8, 8, 8, 64, 16, 33, partition_size=512) == 8 * 8 * 2 * rec(1, 64)
+    assert pkv.decode_workspace_size(256, 32, 8, 128, 16, 512, 512) == 256 * 8 * 16 * rec(4, 128)
+    # 40 heads per kv head: matrix-core chunks of 32 give 2 x 32 head slots
+    assert pkv.decode_workspace_size(2, 40, 1, 64, 16, 64, 256) == 2 * 1 * 4 * 64 * (64 + 2) * 4
     assert pkv.decode_partition_size(1, 1, 1, 64, 16, 8, 48) == 48
     with pytest.raises(pkv.PkvError):
         pkv.decode_partition_size(1, 1, 1, 64, 16, 8, 40)  # not a multiple of the block size

@@ -197,3 +197,24 @@ def test_streams_are_honoured():
         pkv.paged_attention_decode(out, q, kc, vc, bt, cl, case.scale)
     s.synchronize()
     check_close(out, oracle_decode_case(case), "bf16", "side stream")
+
+
+@pytest.mark.parametrize("depth", ["2", "3"])
+@pytest.mark.parametrize("dtype,G,Hkv,D,ctx", [
+    ("bf16", 4, 1, 128, [50000]),               # one stream cut into pieces by every wave
+    ("bf16", 4, 8, 128, [0, 3, 0, 900, 0]),     # empty contexts between live ones
+    ("f16", 1, 2, 64, [1] * 40 + [5000]),       # many one-block streams, one long
+    ("bf16", 32, 1, 128, [20000, 17, 4096]),
+    ("bf16", 40, 2, 64, [3000, 33]),            # heads per kv head above one 32-head chunk
+    ("f32", 2, 2, 64, [7000, 0, 16]),
+])
+def test_balanced_split_edges(depth, dtype, G, Hkv, D, ctx, monkeypatch):
+    """The load-balanced schedule: streams split across many waves, empty streams,
+    waves with no work, and both prefetch depths."""
+    monkeypatch.setenv("PKV_SPLIT_DEPTH", depth)
+    case = make_decode_case([34, G, len(ctx)], dtype, ctx, G * Hkv, Hkv, D)
+    out = run_decode(case, partition_size=0)
+    check_close(out, oracle_decode_case(case), dtype, f"split depth {depth}")
+    for s, n in enumerate(ctx):
+        if n == 0:
+            assert torch.all(out[s] == 0)
