@@ -71,9 +71,9 @@ struct MfmaLoop {
         const char* kt = (const char*)kc + tile_index * (kBlockSize * D * 2) + koff;
         const char* vt = (const char*)vc + tile_index * (kBlockSize * D * 2) + voff;
 #pragma unroll
-        for (int ks = 0; ks < KS; ++ks) t.k[ks] = *(const uint4*)(kt + ks * 64);
+        for (int ks = 0; ks < KS; ++ks) t.k[ks] = stream_load16(kt + ks * 64);
 #pragma unroll
-        for (int dt = 0; dt < DT; ++dt) t.v[dt] = *(const uint2*)(vt + dt * 512);
+        for (int dt = 0; dt < DT; ++dt) t.v[dt] = stream_load8(vt + dt * 512);
     }
 
     // fold one block whose first `valid` tokens are inside the context
@@ -167,8 +167,11 @@ struct MfmaLoop {
 
 // ---------------------------------------------------------------------------------------
 // Vector-ALU inner loop (fp32, or few query heads per kv head).  Four lanes per
-// token share its dot products (shuffle reductions); for P.V each lane owns
-// D/64 head_dim rows of the head_dim-major V tile and all 16 tokens of them.
+// token share its dot products (shuffle reductions).  For P.V every load
+// instruction reads 1 KiB of the head_dim-major V tile contiguously: lane l's
+// piece c is 16-byte chunk c*64+l, i.e. VE tokens of head_dim row (c*64+l)/CPR.
+// Each lane keeps partial sums for its rows over its tokens; the CPR lanes that
+// share a row are added together once, at the end.
 // ---------------------------------------------------------------------------------------
 template <int K> __device__ __forceinline__ void widen16(uint4 c, float* f) {
     if constexpr (K == KF32) {
@@ -191,26 +194,27 @@ struct ValuLoop {
     static constexpr int EB = Elem<K>::bytes;
     static constexpr int VE = 16 / EB;                 // elements per 16-byte chunk
     static constexpr int KC = D / VE / 4;              // K chunks per lane
-    static constexpr int DR = D / 64;                  // output rows per lane
-    static constexpr int VC = DR * kBlockSize * EB / 16;  // V chunks per lane
+    static constexpr int CPR = kBlockSize / VE;        // V chunks per head_dim row (2 or 4)
+    static constexpr int VC = D * CPR / 64;            // V chunks per lane
     static constexpr int HT = GT;
-    static constexpr int kWaves = (D == 128 && (EB == 4 || GT == 4)) ? 1 : 2;
+    static constexpr int kWaves = ((D == 128 && (EB == 4 || GT >= 2)) || (EB == 4 && GT == 4)) ? 1 : 2;
 
     struct Tile {
         uint4 k[KC];
         uint4 v[VC];
     };
     struct State {
-        float m[GT], l[GT], acc[GT][DR];
+        float m[GT], l[GT], acc[GT][VC];
         float q[GT][KC * VE];
     };
 
-    int lane, tq, sub;
+    int lane, tq, sub, tg;
 
     __device__ __forceinline__ void init_lane(int ln) {
         lane = ln;
         tq = ln >> 2;
         sub = ln & 3;
+        tg = ln % CPR;  // which VE tokens of a V row this lane holds
     }
 
     __device__ __forceinline__ void start(State& st, const void* q, size_t qrow, int Hq, int head0, int nh) {
@@ -226,18 +230,18 @@ struct ValuLoop {
             st.m[j] = kNegInf;
             st.l[j] = 0.f;
 #pragma unroll
-            for (int r = 0; r < DR; ++r) st.acc[j][r] = 0.f;
+            for (int c = 0; c < VC; ++c) st.acc[j][c] = 0.f;
         }
     }
 
     __device__ __forceinline__ void load(Tile& t, const void* kc, const void* vc, size_t tile_index) const {
         const size_t base = tile_index * (size_t)(kBlockSize * D * EB);
         const char* kt = (const char*)kc + base + (size_t)tq * D * EB;
-        const char* vt = (const char*)vc + base + (size_t)lane * DR * kBlockSize * EB;
+        const char* vt = (const char*)vc + base + (size_t)lane * 16;
 #pragma unroll
-        for (int k = 0; k < KC; ++k) t.k[k] = *(const uint4*)(kt + (sub + 4 * k) * 16);
+        for (int k = 0; k < KC; ++k) t.k[k] = stream_load16(kt + (sub + 4 * k) * 16);
 #pragma unroll
-        for (int c = 0; c < VC; ++c) t.v[c] = *(const uint4*)(vt + c * 16);
+        for (int c = 0; c < VC; ++c) t.v[c] = stream_load16(vt + c * 1024);
     }
 
     __device__ __forceinline__ void block(State& st, Tile& t, int valid, float scale_log2) const {
@@ -263,45 +267,57 @@ struct ValuLoop {
             st.l[j] = st.l[j] * alpha + (sub == 0 ? pj[j] : 0.f);
             st.m[j] = mn;
 #pragma unroll
-            for (int r = 0; r < DR; ++r) st.acc[j][r] *= alpha;
+            for (int c = 0; c < VC; ++c) st.acc[j][c] *= alpha;
         }
-        float vf[DR * kBlockSize];  // vf[r * 16 + token]
+        float vf[VC][VE];
 #pragma unroll
-        for (int c = 0; c < VC; ++c) widen16<K>(t.v[c], &vf[c * VE]);
+        for (int c = 0; c < VC; ++c) widen16<K>(t.v[c], vf[c]);
         if (valid < kBlockSize) {
 #pragma unroll
-            for (int r = 0; r < DR; ++r)
+            for (int e = 0; e < VE; ++e)
+                if (tg * VE + e >= valid)
 #pragma unroll
-                for (int tk = 0; tk < kBlockSize; ++tk)
-                    if (tk >= valid) vf[r * kBlockSize + tk] = 0.f;
+                    for (int c = 0; c < VC; ++c) vf[c][e] = 0.f;
         }
 #pragma unroll
         for (int j = 0; j < GT; ++j) {
+            float ps[kBlockSize];  // p of every token of the block (wave-uniform)
 #pragma unroll
-            for (int tk = 0; tk < kBlockSize; ++tk) {
-                const float pt = read_lane(pj[j], 4 * tk);
+            for (int tk = 0; tk < kBlockSize; ++tk) ps[tk] = read_lane(pj[j], 4 * tk);
 #pragma unroll
-                for (int r = 0; r < DR; ++r) st.acc[j][r] = fmaf(pt, vf[r * kBlockSize + tk], st.acc[j][r]);
+            for (int e = 0; e < VE; ++e) {
+                float pe = ps[e];
+#pragma unroll
+                for (int g = 1; g < CPR; ++g) pe = tg == g ? ps[g * VE + e] : pe;
+#pragma unroll
+                for (int c = 0; c < VC; ++c) st.acc[j][c] = fmaf(pe, vf[c][e], st.acc[j][c]);
             }
         }
     }
 
     __device__ __forceinline__ void finish(State& st) const {
 #pragma unroll
-        for (int j = 0; j < GT; ++j)
+        for (int j = 0; j < GT; ++j) {
 #pragma unroll
             for (int mask = 1; mask < 64; mask <<= 1) st.l[j] = xor_sum(st.l[j], mask);
+#pragma unroll
+            for (int c = 0; c < VC; ++c)
+#pragma unroll
+                for (int mask = 1; mask < CPR; mask <<= 1) st.acc[j][c] = xor_sum(st.acc[j][c], mask);
+        }
     }
+
+    __device__ __forceinline__ int row(int c) const { return (c * 64 + lane) / CPR; }
 
     __device__ __forceinline__ void store_out(const State& st, void* out, size_t orow, int Hq, int head0,
                                               int nh) const {
+        if (tg != 0) return;
 #pragma unroll
         for (int j = 0; j < GT; ++j) {
             if (j >= nh) continue;
             const float inv = st.l[j] > 0.f ? 1.f / st.l[j] : 0.f;
 #pragma unroll
-            for (int r = 0; r < DR; ++r)
-                store_elem<K>(out, (orow * Hq + head0 + j) * D + lane * DR + r, st.acc[j][r] * inv);
+            for (int c = 0; c < VC; ++c) store_elem<K>(out, (orow * Hq + head0 + j) * D + row(c), st.acc[j][c] * inv);
         }
     }
 
@@ -309,8 +325,10 @@ struct ValuLoop {
 #pragma unroll
         for (int j = 0; j < GT; ++j) {
             if (j >= nh) continue;
+            if (tg == 0) {
 #pragma unroll
-            for (int r = 0; r < DR; ++r) rec[j * D + lane * DR + r] = st.acc[j][r];
+                for (int c = 0; c < VC; ++c) rec[j * D + row(c)] = st.acc[j][c];
+            }
             if (lane == 0) {
                 rec[cap * D + j] = st.m[j];
                 rec[cap * D + cap + j] = st.l[j];

@@ -13,6 +13,8 @@ typedef _Float16 f16x4 __attribute__((ext_vector_type(4)));
 typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
 
 // Element kinds.  Storage is always raw bits; arithmetic is fp32.
 enum Kind { KF32 = 0, KF16 = 1, KBF16 = 2 };
@@ -81,6 +83,18 @@ template <> __device__ __forceinline__ f32x4 mma_16x16x16<KBF16>(uint2 a, uint2 
 template <> __device__ __forceinline__ f32x4 mma_16x16x16<KF16>(uint2 a, uint2 b, f32x4 c) {
     return __builtin_amdgcn_mfma_f32_16x16x16f16(__builtin_bit_cast(f16x4, a), __builtin_bit_cast(f16x4, b), c, 0,
                                                  0, 0);
+}
+
+// ---- streaming loads -----------------------------------------------------------------
+// K/V tiles are read exactly once per call: load them with the non-temporal hint
+// so they do not displace reused data in the caches.
+__device__ __forceinline__ uint4 stream_load16(const void* p) {
+    const u32x4 x = __builtin_nontemporal_load((const u32x4*)p);
+    return make_uint4(x.x, x.y, x.z, x.w);
+}
+__device__ __forceinline__ uint2 stream_load8(const void* p) {
+    const u32x2 x = __builtin_nontemporal_load((const u32x2*)p);
+    return make_uint2(x.x, x.y);
 }
 
 // ---- misc ------------------------------------------------------------------------------
