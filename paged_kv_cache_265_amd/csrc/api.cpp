@@ -58,6 +58,9 @@ int max_parts(int max_blocks_per_seq, int part) {
     return (int)((tokens + part - 1) / part);
 }
 
+// balanced split: the per-sequence start units (S + 1 int64) precede the records
+size_t split_prefix_bytes(int num_seqs) { return (((size_t)num_seqs + 1) * 8 + 255) / 256 * 256; }
+
 // Largest (query-head chunks x record capacity) over the inner loops a decode
 // with G heads per kv head may use, and the largest record capacity.
 void record_shape(int G, long long* heads_per_kv, int* cap_max) {
@@ -126,7 +129,7 @@ size_t pkv_decode_workspace_size(int num_seqs, int num_q_heads, int num_kv_heads
     int cap = 0;
     record_shape(G, &heads_per_kv, &cap);
     const size_t per_head = ((size_t)head_dim + 2) * sizeof(float);
-    if (partition_size == 0) return (size_t)pkv::kMaxSplitWaves * 2 * cap * per_head;
+    if (partition_size == 0) return split_prefix_bytes(num_seqs) + (size_t)pkv::kMaxSplitWaves * 2 * cap * per_head;
     const int mp = max_parts(max_blocks_per_seq, partition_size);
     if (mp <= 1) return 0;
     return (size_t)num_seqs * num_kv_heads * heads_per_kv * mp * per_head;
@@ -177,7 +180,13 @@ int paged_attention_decode(void* out, const void* query, const void* key_cache, 
     p.vc = value_cache;
     p.block_tables = block_tables;
     p.context_lens = context_lens;
-    p.ws = (float*)workspace;
+    if (partition_size == 0) {
+        p.starts = (long long*)workspace;
+        p.ws = (float*)((char*)workspace + split_prefix_bytes(num_seqs));
+    } else {
+        p.starts = nullptr;
+        p.ws = (float*)workspace;
+    }
     p.S = num_seqs;
     p.Hq = num_q_heads;
     p.Hkv = num_kv_heads;

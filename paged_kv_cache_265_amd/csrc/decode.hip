@@ -90,6 +90,9 @@ __global__ __launch_bounds__(64, Loop::kWaves) void decode_split(DecodeParams p)
     const int NS = p.Hkv * p.chunks;
     const long long U = total_blocks(p, lane) * NS;
     const long long lo = w * U / N, hi = (w + 1) * U / N;
+    // starts[s] = unit of sequence s's first block (written by the wave that folds
+    // it), starts[S] = U: the merge finds every stream's pieces from these
+    if (w == 0 && lane == 0) p.starts[p.S] = U;
     if (lo >= hi) return;
 
     // locate unit lo: sequence s whose units [NS*cum(s), NS*cum(s+1)) contain it
@@ -152,6 +155,7 @@ __global__ __launch_bounds__(64, Loop::kWaves) void decode_split(DecodeParams p)
         }
     };
     auto compute = [&](typename Loop::Tile& t) {
+        if (cc.b == 0 && cc.c == 0 && lane == 0) p.starts[cc.s] = lo + done;
         if (done == 0 || cc.b == 0) {
             seg_b0 = cc.b;
             hd = stream_heads<HT>(p, cc.c);
@@ -247,7 +251,6 @@ __global__ __launch_bounds__(64) void decode_fixed(DecodeParams p) {
 // ---------------------------------------------------------------------------------------
 template <int K, int HT>
 __global__ __launch_bounds__(256) void decode_merge(DecodeParams p, int split_waves) {
-    __shared__ long long red[8];
     const int NS = p.Hkv * p.chunks;
     const int stream = blockIdx.x;
     const int s = stream / NS;
@@ -274,27 +277,8 @@ __global__ __launch_bounds__(256) void decode_merge(DecodeParams p, int split_wa
                 store_elem<K>(p.out, ((size_t)s * p.Hq + hd.head0) * D + e, 0.f);
             return;
         }
-        // total blocks and blocks before sequence s
-        long long tot = 0, before = 0;
-        for (int i = threadIdx.x; i < p.S; i += blockDim.x) {
-            const int n = nblocks(p.context_lens[i]);
-            tot += n;
-            if (i < s) before += n;
-        }
-#pragma unroll
-        for (int m = 1; m < 64; m <<= 1) {
-            tot += __shfl_xor(tot, m, 64);
-            before += __shfl_xor(before, m, 64);
-        }
-        if ((threadIdx.x & 63) == 0) {
-            red[threadIdx.x >> 6] = tot;
-            red[4 + (threadIdx.x >> 6)] = before;
-        }
-        __syncthreads();
-        tot = red[0] + red[1] + red[2] + red[3];
-        before = red[4] + red[5] + red[6] + red[7];
-        U = tot * NS;
-        a = before * NS + (long long)c * nb;
+        U = p.starts[p.S];
+        a = p.starts[s] + (long long)c * nb;
         const long long e = a + nb;
         w0 = wave_of(a, U, N);
         const long long w1 = wave_of(e - 1, U, N);
@@ -312,16 +296,38 @@ __global__ __launch_bounds__(256) void decode_merge(DecodeParams p, int split_wa
         const long long w = U >= N ? w0 + i : wave_of(a + i, U, N);
         return p.ws + (size_t)w * 2 * rec;  // slot 0: that wave's first segment
     };
+    // one pass over the pieces, eight at a time so that their loads are in flight
+    // together: (M, L, O) folded online, rescaled by 2^(M_old - M_new)
+    constexpr int CH = 8;
     for (int e = threadIdx.x; e < hd.nh * D; e += blockDim.x) {
         const int h = e / D, d = e - h * D;
-        float M = kNegInf;
-        for (long long i = 0; i < count; ++i) M = fmaxf(M, record(i)[cap * D + h]);
-        float L = 0.f, O = 0.f;
-        for (long long i = 0; i < count; ++i) {
-            const float* r = record(i);
-            const float wt = fast_exp2(r[cap * D + h] - M);
-            L += wt * r[cap * D + cap + h];
-            O += wt * r[h * D + d];
+        float M = kNegInf, L = 0.f, O = 0.f;
+        for (long long i0 = 0; i0 < count; i0 += CH) {
+            float mv[CH], lv[CH], av[CH];
+#pragma unroll
+            for (int j = 0; j < CH; ++j) {
+                mv[j] = kNegInf;
+                lv[j] = av[j] = 0.f;
+                if (i0 + j < count) {
+                    const float* r = record(i0 + j);
+                    mv[j] = r[cap * D + h];
+                    lv[j] = r[cap * D + cap + h];
+                    av[j] = r[h * D + d];
+                }
+            }
+            float mn = M;
+#pragma unroll
+            for (int j = 0; j < CH; ++j) mn = fmaxf(mn, mv[j]);
+            const float sc = fast_exp2(M - mn);
+            L *= sc;
+            O *= sc;
+#pragma unroll
+            for (int j = 0; j < CH; ++j) {
+                const float wt = fast_exp2(mv[j] - mn);
+                L += wt * lv[j];
+                O += wt * av[j];
+            }
+            M = mn;
         }
         store_elem<K>(p.out, ((size_t)s * p.Hq + hd.head0 + h) * D + d, L > 0.f ? O / L : 0.f);
     }

@@ -19,6 +19,7 @@ struct DecodeParams {
     const int32_t* block_tables;
     const int32_t* context_lens;
     float* ws;        // partial records: acc[cap][D], m[cap], l[cap] (m in log2 units)
+    long long* starts;  // balanced split: first unit of every sequence, then the unit count
     int S, Hq, Hkv, G, D, NB, MB;
     int chunks;       // query-head chunks per kv head (set by the launcher)
     int part_tokens;  // 0: balanced split; else tokens per fixed partition (multiple of kBlockSize)
