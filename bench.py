@@ -279,6 +279,19 @@ def run_long(args, p, qd, qc, cu, torch, pkv, workloads, dev):
     ms_step = (time.perf_counter() - t0) * 1e3 / args.steps
     dec_ms = float(np.mean([a.elapsed_time(b) for a, b, c in evs]))
     chk_ms = float(np.mean([b.elapsed_time(c) for a, b, c in evs]))
+    # the same decode with the library's balanced split instead of 512-token partitions
+    wsb = torch.zeros(pkv.decode_workspace_size(S, 32, 1, 128, 16, p.block_tables.shape[1], 0), dtype=torch.uint8,
+                      device=dev)
+    outb = torch.empty_like(q)
+    for _ in range(args.warmup):
+        pkv.paged_attention_decode(outb, q, kc, vc, bt[:S], cl[:S], scale, partition_size=0, workspace=wsb)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(args.steps):
+        pkv.paged_attention_decode(outb, q, kc, vc, bt[:S], cl[:S], scale, partition_size=0, workspace=wsb)
+    e1.record()
+    torch.cuda.synchronize()
+    bal_ms = e0.elapsed_time(e1) / args.steps
     nbytes = workloads.algorithmic_decode_bytes(p.context_lens[:S], 32, 1, 128, 2)
     flops = workloads.algorithmic_chunked_flops(p.context_lens[S:], np.diff(cu), 32, 128)
     res = {"metric": METRIC, "value": round(nbytes / (dec_ms * 1e-3) / 1e9, 1), "unit": "GB/s", "n_gpus": 1,
@@ -288,6 +301,8 @@ def run_long(args, p, qd, qc, cu, torch, pkv, workloads, dev):
                                   "[16384, 131072], 512-token partitions) + 8 chunked-prefill segments of 512 "
                                   "rows over 4096 cached tokens"},
            "decode_ms": round(dec_ms, 4), "chunked_ms": round(chk_ms, 4),
+           "decode_balanced_split_ms": round(bal_ms, 4),
+           "decode_balanced_split_GBs": round(nbytes / (bal_ms * 1e-3) / 1e9, 1),
            "chunked_tflops": round(flops / (chk_ms * 1e-3) / 1e12, 2),
            "roofline": {"bound": "hbm", "kernel": "paged_attention_decode", "achieved":
                         round(nbytes / (dec_ms * 1e-3) / 1e9, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",

@@ -15,10 +15,10 @@
 //    units in (sequence, stream, block) order.  It walks them with two blocks in
 //    flight, writes the normalised output of every stream it covers whole, and
 //    leaves (m, l, acc) records for the at most two streams it covers in part (its
-//    first and its last).  decode_merge joins the pieces of split streams.
+//    first and its last).  A merge kernel joins the pieces of split streams.
 //  * fixed partitions (partition_size > 0): one wave per (stream, partition of
 //    partition_size tokens); multi-partition streams leave one record per
-//    partition for decode_merge.
+//    partition for the merge kernel.
 #include "decode_inner.h"
 #include "device.h"
 #include "internal.h"
@@ -247,10 +247,12 @@ __global__ __launch_bounds__(64) void decode_fixed(DecodeParams p) {
 }
 
 // ---------------------------------------------------------------------------------------
-// merge of the pieces of a stream: o = sum_i 2^(m_i - M) acc_i / sum_i 2^(m_i - M) l_i
+// balanced split, streams of few query heads: one workgroup per stream merges
+// all its heads, o = sum_i 2^(m_i - M) acc_i / sum_i 2^(m_i - M) l_i.  Sequences
+// with an empty context get their zero output here.
 // ---------------------------------------------------------------------------------------
 template <int K, int HT>
-__global__ __launch_bounds__(256) void decode_merge(DecodeParams p, int split_waves) {
+__global__ __launch_bounds__(256) void decode_merge_stream(DecodeParams p, int split_waves) {
     const int NS = p.Hkv * p.chunks;
     const int stream = blockIdx.x;
     const int s = stream / NS;
@@ -334,6 +336,159 @@ __global__ __launch_bounds__(256) void decode_merge(DecodeParams p, int split_wa
 }
 
 // ---------------------------------------------------------------------------------------
+// merge of the pieces of a stream, one query head per workgroup:
+//   o = sum_i 2^(m_i - M) acc_i / sum_i 2^(m_i - M) l_i.
+// Pieces: the fixed partitions 0 .. nparts-1 of the stream, or, for the balanced
+// split, the waves w0 .. w1 whose unit ranges cut the stream (w0's last record,
+// then slot 0 of the others; when U < N each unit sits alone in its own wave).
+// 256 threads = 2 groups x 128 head_dim lanes; group g folds pieces g, g+2, ...
+// with the weights 2^(m_i - M) taken from LDS.  Balanced split only: sequences
+// with an empty context get their zero output here.
+// ---------------------------------------------------------------------------------------
+template <int K, int HT>
+__global__ __launch_bounds__(256) void decode_merge_head(DecodeParams p, int split_waves) {
+    constexpr int kRound = 1024;  // pieces folded per round
+    __shared__ const float* ptr[kRound];
+    __shared__ float wts[kRound];
+    __shared__ float red[8];
+    __shared__ float part_o[128];
+    const int NS = p.Hkv * p.chunks;
+    const int cap = min(p.G, HT);
+    int idx = blockIdx.x;
+    const int h = idx % cap;
+    idx /= cap;
+    const int c = idx % NS;
+    const int s = idx / NS;
+    const Heads hd = stream_heads<HT>(p, c);
+    if (h >= hd.nh) return;
+    const int ctx = p.context_lens[s];
+    const int D = p.D;
+    const size_t rec = (size_t)cap * (D + 2);
+    const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+
+    long long count, w0 = 0, U = 0, a = 0;
+    const long long N = split_waves;
+    const float* first;
+    if (split_waves == 0) {
+        count = ctx > 0 ? (ctx + p.part_tokens - 1) / p.part_tokens : 1;
+        if (count <= 1) return;
+        first = p.ws + (size_t)(s * NS + c) * p.max_parts * rec;
+    } else {
+        const int nb = nblocks(ctx);
+        if (nb == 0) {
+            for (int d = tid; d < D; d += 256) store_elem<K>(p.out, ((size_t)s * p.Hq + hd.head0 + h) * D + d, 0.f);
+            return;
+        }
+        U = p.starts[p.S];
+        a = p.starts[s] + (long long)c * nb;
+        w0 = wave_of(a, U, N);
+        const long long w1 = wave_of(a + nb - 1, U, N);
+        if (w0 == w1) return;  // written whole by one wave
+        first = p.ws + ((size_t)w0 * 2 + (w0 * U / N == a ? 0 : 1)) * rec;  // w0's last segment
+        count = U >= N ? w1 - w0 + 1 : nb;
+    }
+    auto record = [&](long long i) -> const float* {
+        if (split_waves == 0) return first + i * rec;
+        if (i == 0) return first;
+        return p.ws + (size_t)(U >= N ? w0 + i : wave_of(a + i, U, N)) * 2 * rec;
+    };
+    float M = kNegInf;
+    for (long long i = tid; i < count; i += 256) M = fmaxf(M, record(i)[cap * D + h]);
+#pragma unroll
+    for (int m = 1; m < 64; m <<= 1) M = fmaxf(M, __shfl_xor(M, m, 64));
+    if (lane == 0) red[wv] = M;
+    __syncthreads();
+    M = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
+    float L = 0.f, O = 0.f;
+    const int g = tid >> 7, d = tid & 127;
+    for (long long r0 = 0; r0 < count; r0 += kRound) {
+        const int n = (int)min((long long)kRound, count - r0);
+        __syncthreads();
+        for (int i = tid; i < n; i += 256) {
+            const float* r = record(r0 + i);
+            const float w = fast_exp2(r[cap * D + h] - M);
+            ptr[i] = r;
+            wts[i] = w;
+            L += w * r[cap * D + cap + h];
+        }
+        __syncthreads();
+        if (d < D) {
+#pragma unroll 16
+            for (int i = g; i < n; i += 2) O += wts[i] * ptr[i][h * D + d];
+        }
+    }
+#pragma unroll
+    for (int m = 1; m < 64; m <<= 1) L += __shfl_xor(L, m, 64);
+    if (lane == 0) red[4 + wv] = L;
+    if (g == 1) part_o[d] = O;
+    __syncthreads();
+    L = red[4] + red[5] + red[6] + red[7];
+    if (g == 0 && d < D)
+        store_elem<K>(p.out, ((size_t)s * p.Hq + hd.head0 + h) * D + d, L > 0.f ? (O + part_o[d]) / L : 0.f);
+}
+
+// ---------------------------------------------------------------------------------------
+// fixed partitions: merge of one query head of one stream per workgroup (streams
+// can have hundreds of partitions).  256 threads = 2 groups x 128 head_dim lanes;
+// group g folds partitions g, g+2, ...; the weights 2^(m_i - M) come from LDS.
+// ---------------------------------------------------------------------------------------
+template <int K, int HT>
+__global__ __launch_bounds__(256) void decode_merge_fixed(DecodeParams p) {
+    constexpr int kRound = 1024;  // partitions folded per round
+    __shared__ float wts[kRound];
+    __shared__ float red[8];
+    __shared__ float part_o[128];
+    const int NS = p.Hkv * p.chunks;
+    const int cap = min(p.G, HT);
+    int idx = blockIdx.x;
+    const int h = idx % cap;
+    idx /= cap;
+    const int c = idx % NS;
+    const int s = idx / NS;
+    const Heads hd = stream_heads<HT>(p, c);
+    if (h >= hd.nh) return;
+    const int ctx = p.context_lens[s];
+    const int nparts = ctx > 0 ? (ctx + p.part_tokens - 1) / p.part_tokens : 1;
+    if (nparts <= 1) return;
+    const int D = p.D;
+    const size_t rec = (size_t)cap * (D + 2);
+    const float* base = p.ws + (size_t)(s * NS + c) * p.max_parts * rec;
+    const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+    float M = kNegInf;
+    for (int i = tid; i < nparts; i += 256) M = fmaxf(M, base[i * rec + cap * D + h]);
+#pragma unroll
+    for (int m = 1; m < 64; m <<= 1) M = fmaxf(M, __shfl_xor(M, m, 64));
+    if (lane == 0) red[wv] = M;
+    __syncthreads();
+    M = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
+    float L = 0.f, O = 0.f;
+    const int g = tid >> 7, d = tid & 127;
+    for (int r0 = 0; r0 < nparts; r0 += kRound) {
+        const int n = min(kRound, nparts - r0);
+        __syncthreads();
+        for (int i = tid; i < n; i += 256) {
+            const float* r = base + (size_t)(r0 + i) * rec;
+            const float w = fast_exp2(r[cap * D + h] - M);
+            wts[i] = w;
+            L += w * r[cap * D + cap + h];
+        }
+        __syncthreads();
+        if (d < D) {
+#pragma unroll 16
+            for (int i = g; i < n; i += 2) O += wts[i] * base[(size_t)(r0 + i) * rec + h * D + d];
+        }
+    }
+#pragma unroll
+    for (int m = 1; m < 64; m <<= 1) L += __shfl_xor(L, m, 64);
+    if (lane == 0) red[4 + wv] = L;
+    if (g == 1) part_o[d] = O;
+    __syncthreads();
+    L = red[4] + red[5] + red[6] + red[7];
+    if (g == 0 && d < D)
+        store_elem<K>(p.out, ((size_t)s * p.Hq + hd.head0 + h) * D + d, L > 0.f ? (O + part_o[d]) / L : 0.f);
+}
+
+// ---------------------------------------------------------------------------------------
 // host side
 // ---------------------------------------------------------------------------------------
 
@@ -379,9 +534,16 @@ hipError_t run(const DecodeParams& p0, bool split, int slot, hipStream_t st) {
         hipLaunchKernelGGL(decode_fixed<Loop>, dim3((unsigned)grid), dim3(64), 0, st, p);
     }
     hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return e;
-    if (!split && p.max_parts <= 1) return hipSuccess;
-    hipLaunchKernelGGL((decode_merge<K, Loop::HT>), dim3((unsigned)(p.S * NS)), dim3(256), 0, st, p, waves);
+    if (e != hipSuccess || (!split && p.max_parts <= 1)) return e;
+    // few heads per stream: a workgroup per stream; many (MQA-like): one per head
+    const int cap = p.G < Loop::HT ? p.G : Loop::HT;
+    const unsigned per_head = (unsigned)((long long)p.S * NS * cap);
+    if (!split)
+        hipLaunchKernelGGL((decode_merge_fixed<K, Loop::HT>), dim3(per_head), dim3(256), 0, st, p);
+    else if (cap <= 8)
+        hipLaunchKernelGGL((decode_merge_stream<K, Loop::HT>), dim3((unsigned)(p.S * NS)), dim3(256), 0, st, p, waves);
+    else
+        hipLaunchKernelGGL((decode_merge_head<K, Loop::HT>), dim3(per_head), dim3(256), 0, st, p, waves);
     return hipGetLastError();
 }
 

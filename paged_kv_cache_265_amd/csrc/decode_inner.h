@@ -96,9 +96,12 @@ struct MfmaLoop {
 #pragma unroll
             for (int j = 0; j < 4; ++j) pr[j] = fast_exp2(sv[j] - mn);
             st.l[ht] = st.l[ht] * alpha + ((pr[0] + pr[1]) + (pr[2] + pr[3]));
-            st.m[ht] = mn;
+            // rescaling by alpha = 1 changes nothing: skip it when no lane's max moved
+            if (__ballot(mn != st.m[ht])) {
 #pragma unroll
-            for (int dt = 0; dt < DT; ++dt) st.acc[ht][dt] *= alpha;
+                for (int dt = 0; dt < DT; ++dt) st.acc[ht][dt] *= alpha;
+            }
+            st.m[ht] = mn;
             phi[ht] = pack4<K>(pr[0], pr[1], pr[2], pr[3]);
             plo[ht] = pack4<K>(pr[0] - lo16<K>(phi[ht].x), pr[1] - hi16<K>(phi[ht].x), pr[2] - lo16<K>(phi[ht].y),
                                pr[3] - hi16<K>(phi[ht].y));
@@ -265,9 +268,11 @@ struct ValuLoop {
             const float alpha = fast_exp2(st.m[j] - mn);
             pj[j] = fast_exp2(sv - mn);
             st.l[j] = st.l[j] * alpha + (sub == 0 ? pj[j] : 0.f);
-            st.m[j] = mn;
+            if (__ballot(mn != st.m[j])) {  // alpha = 1 everywhere otherwise
 #pragma unroll
-            for (int c = 0; c < VC; ++c) st.acc[j][c] *= alpha;
+                for (int c = 0; c < VC; ++c) st.acc[j][c] *= alpha;
+            }
+            st.m[j] = mn;
         }
         float vf[VC][VE];
 #pragma unroll
