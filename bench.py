@@ -32,7 +32,9 @@ sys.path.insert(0, ROOT)
 METRIC = "paged-attn decode achieved HBM GB/s (% of MI355X peak) + sequences/sec"
 PEAK_HBM_GBS = 8000.0
 PROFILES = os.path.join(ROOT, "profiles")
-KERNEL_SOURCE = os.path.join(ROOT, "paged_kv_cache_265_amd", "csrc", "decode.hip")
+# sources of the decode kernels: counter summaries are valid only for these exact files
+KERNEL_SOURCES = [os.path.join(ROOT, "paged_kv_cache_265_amd", "csrc", f)
+                  for f in ("decode.hip", "decode_inner.h", "device.h", "internal.h")]
 
 
 def log(msg):
@@ -40,7 +42,10 @@ def log(msg):
 
 
 def source_sha() -> str:
-    return hashlib.sha256(open(KERNEL_SOURCE, "rb").read()).hexdigest()[:16]
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES:
+        h.update(open(f, "rb").read())
+    return h.hexdigest()[:16]
 
 
 def traffic_from_profiles(workload: str):
