@@ -127,7 +127,7 @@ __global__ __launch_bounds__(64, Loop::kWaves) void decode_split(DecodeParams p)
         x.c = 0;
         do {
             ++x.s;
-            x.ctx = x.s < p.S ? p.context_lens[x.s] : BS;
+            x.ctx = x.s < p.S ? scalar_load(p.context_lens, uniform(x.s)) : BS;
             x.nb = nblocks(x.ctx);
         } while (x.nb == 0);
     };
@@ -146,10 +146,13 @@ __global__ __launch_bounds__(64, Loop::kWaves) void decode_split(DecodeParams p)
     bool first_seg = true;
     Heads hd = stream_heads<HT>(p, cur.c);
 
+    // every call issues the loads of one tile -- a real one while units remain,
+    // else an empty one -- so the wait before each fold covers exactly its own tile
     auto issue = [&](typename Loop::Tile& t) {
-        if (issued < cnt) {
-            const int phys = p.block_tables[(size_t)ac.s * p.MB + ac.b];
-            L.load(t, p.kc, p.vc, (size_t)phys * p.Hkv + ac.c / p.chunks);
+        const bool live = issued < cnt;
+        const int phys = live ? scalar_load(p.block_tables, (size_t)uniform(ac.s) * p.MB + uniform(ac.b)) : 0;
+        L.load(t, p.kc, p.vc, (size_t)phys * p.Hkv + ac.c / p.chunks, live);
+        if (live) {
             advance(ac);
             ++issued;
         }
@@ -160,6 +163,7 @@ __global__ __launch_bounds__(64, Loop::kWaves) void decode_split(DecodeParams p)
             seg_b0 = cc.b;
             hd = stream_heads<HT>(p, cc.c);
             L.start(st, p.q, cc.s, p.Hq, hd.head0, hd.nh);
+            vm_wait_all();  // the query loads complete on this path only
         }
         L.block(st, t, cc.ctx - cc.b * BS, p.scale_log2);
         if (done + 1 == cnt || cc.b + 1 == cc.nb) {
@@ -203,7 +207,7 @@ __global__ __launch_bounds__(64, Loop::kWaves) void decode_split(DecodeParams p)
 // fixed partitions
 // ---------------------------------------------------------------------------------------
 template <class Loop>
-__global__ __launch_bounds__(64) void decode_fixed(DecodeParams p) {
+__global__ __launch_bounds__(64, Loop::kWaves) void decode_fixed(DecodeParams p) {
     constexpr int HT = Loop::HT;
     const int NS = p.Hkv * p.chunks;
     int idx = blockIdx.x;
@@ -224,17 +228,24 @@ __global__ __launch_bounds__(64) void decode_fixed(DecodeParams p) {
     L.init_lane(lane_id());
     typename Loop::State st;
     L.start(st, p.q, s, p.Hq, hd.head0, hd.nh);
-    const int32_t* table = p.block_tables + (size_t)s * p.MB;
-    typename Loop::Tile ta, tb;
-    auto load = [&](int i, typename Loop::Tile& t) {
-        L.load(t, p.kc, p.vc, (size_t)table[b0 + i] * p.Hkv + hd.kvh);
+    // two blocks in flight while one is folded; past the end the loads are empty
+    typename Loop::Tile ta, tb, tc;
+    auto issue = [&](int i, typename Loop::Tile& t) {
+        const bool live = i < nb;
+        const int phys = live ? scalar_load(p.block_tables, (size_t)s * p.MB + b0 + i) : 0;
+        L.load(t, p.kc, p.vc, (size_t)phys * p.Hkv + hd.kvh, live);
     };
-    if (nb > 0) load(0, ta);
-    for (int i = 0; i < nb; i += 2) {
-        if (i + 1 < nb) load(i + 1, tb);
+    issue(0, ta);
+    issue(1, tb);
+    for (int i = 0; i < nb; i += 3) {
+        issue(i + 2, tc);
         L.block(st, ta, t1 - (b0 + i) * BS, p.scale_log2);
-        if (i + 2 < nb) load(i + 2, ta);
-        if (i + 1 < nb) L.block(st, tb, t1 - (b0 + i + 1) * BS, p.scale_log2);
+        if (i + 1 >= nb) break;
+        issue(i + 3, ta);
+        L.block(st, tb, t1 - (b0 + i + 1) * BS, p.scale_log2);
+        if (i + 2 >= nb) break;
+        issue(i + 4, tb);
+        L.block(st, tc, t1 - (b0 + i + 2) * BS, p.scale_log2);
     }
     L.finish(st);
     if (nparts == 1) {

@@ -67,13 +67,18 @@ struct MfmaLoop {
         }
     }
 
-    __device__ __forceinline__ void load(Tile& t, const void* kc, const void* vc, size_t tile_index) const {
-        const char* kt = (const char*)kc + tile_index * (kBlockSize * D * 2) + koff;
-        const char* vt = (const char*)vc + tile_index * (kBlockSize * D * 2) + voff;
+    // K/V tile `tile_index` of the pools; with live = false the loads return zeros
+    // and read nothing
+    __device__ __forceinline__ void load(Tile& t, const void* kc, const void* vc, size_t tile_index,
+                                         bool live) const {
+        constexpr uint32_t kTile = kBlockSize * D * 2;
+        const size_t base = live ? tile_index * kTile : 0;
+        const rsrc_t kr = tile_rsrc((const char*)kc + base, live ? kTile : 0);
+        const rsrc_t vr = tile_rsrc((const char*)vc + base, live ? kTile : 0);
 #pragma unroll
-        for (int ks = 0; ks < KS; ++ks) t.k[ks] = stream_load16(kt + ks * 64);
+        for (int ks = 0; ks < KS; ++ks) t.k[ks] = stream_load16(kr, koff + ks * 64);
 #pragma unroll
-        for (int dt = 0; dt < DT; ++dt) t.v[dt] = stream_load8(vt + dt * 512);
+        for (int dt = 0; dt < DT; ++dt) t.v[dt] = stream_load8(vr, voff + dt * 512);
     }
 
     // fold one block whose first `valid` tokens are inside the context
@@ -237,14 +242,19 @@ struct ValuLoop {
         }
     }
 
-    __device__ __forceinline__ void load(Tile& t, const void* kc, const void* vc, size_t tile_index) const {
-        const size_t base = tile_index * (size_t)(kBlockSize * D * EB);
-        const char* kt = (const char*)kc + base + (size_t)tq * D * EB;
-        const char* vt = (const char*)vc + base + (size_t)lane * 16;
+    // K/V tile `tile_index` of the pools; with live = false the loads return zeros
+    // and read nothing
+    __device__ __forceinline__ void load(Tile& t, const void* kc, const void* vc, size_t tile_index,
+                                         bool live) const {
+        constexpr uint32_t kTile = kBlockSize * D * EB;
+        const size_t base = live ? tile_index * kTile : 0;
+        const rsrc_t kr = tile_rsrc((const char*)kc + base, live ? kTile : 0);
+        const rsrc_t vr = tile_rsrc((const char*)vc + base, live ? kTile : 0);
+        const uint32_t kt = (uint32_t)(tq * D * EB), vt = (uint32_t)lane * 16;
 #pragma unroll
-        for (int k = 0; k < KC; ++k) t.k[k] = stream_load16(kt + (sub + 4 * k) * 16);
+        for (int k = 0; k < KC; ++k) t.k[k] = stream_load16(kr, kt + (sub + 4 * k) * 16);
 #pragma unroll
-        for (int c = 0; c < VC; ++c) t.v[c] = stream_load16(vt + c * 1024);
+        for (int c = 0; c < VC; ++c) t.v[c] = stream_load16(vr, vt + c * 1024);
     }
 
     __device__ __forceinline__ void block(State& st, Tile& t, int valid, float scale_log2) const {

@@ -97,11 +97,49 @@ __device__ __forceinline__ uint2 stream_load8(const void* p) {
     return make_uint2(x.x, x.y);
 }
 
+// Buffer resource over the `bytes` bytes at `base` (raw, unswizzled; dword 3 as
+// the gfx9 family takes it).  Loads at offsets past `bytes` return zeros and make
+// no memory access, so a pipeline can issue a load on every iteration -- with
+// bytes = 0 once it has run out of tiles -- and the compiler can count exactly
+// which of its loads are still in flight.
+typedef __amdgpu_buffer_rsrc_t rsrc_t;
+__device__ __forceinline__ rsrc_t tile_rsrc(const void* base, uint32_t bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, (int)bytes, 0x00020000);
+}
+constexpr int kNonTemporal = 2;  // cache-policy bit of the buffer loads: nt
+__device__ __forceinline__ uint4 stream_load16(rsrc_t r, uint32_t off) {
+    const u32x4 x = __builtin_amdgcn_raw_buffer_load_b128(r, (int)off, 0, kNonTemporal);
+    return make_uint4(x.x, x.y, x.z, x.w);
+}
+__device__ __forceinline__ uint2 stream_load8(rsrc_t r, uint32_t off) {
+    const u32x2 x = __builtin_amdgcn_raw_buffer_load_b64(r, (int)off, 0, kNonTemporal);
+    return make_uint2(x.x, x.y);
+}
+
 // ---- misc ------------------------------------------------------------------------------
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
 __device__ __forceinline__ int lane_id() { return (int)(threadIdx.x & 63); }
+
+// Assert that v is the same in every lane, so that addresses built from it stay in
+// scalar registers: loads through them are then scalar loads, which the wave waits
+// for separately from its vector loads still in flight.
+__device__ __forceinline__ int uniform(int v) { return __builtin_amdgcn_readfirstlane(v); }
+
+// Wait until every vector memory access of this wave has completed (s_waitcnt
+// vmcnt(0); the expcnt and lgkmcnt fields are left at their maximum).  Placed
+// right after loads made on a rarely taken path, it keeps the compiler from
+// waiting for them -- and with them for everything issued before -- on every
+// path that joins afterwards.
+__device__ __forceinline__ void vm_wait_all() { __builtin_amdgcn_s_waitcnt(0x0F70); }
+
+// Scalar load of base[i] with a wave-uniform i, for tables the kernel only reads
+// (block tables, context lengths): through the constant address space the compiler
+// may use the scalar cache even though the kernel stores elsewhere.
+__device__ __forceinline__ int scalar_load(const int32_t* base, size_t i) {
+    return ((const __attribute__((address_space(4))) int32_t*)base)[i];
+}
 
 // value of a wave-uniform register from lane `src` (src must be wave-uniform)
 __device__ __forceinline__ int read_lane(int v, int src) { return __builtin_amdgcn_readlane(v, src); }
