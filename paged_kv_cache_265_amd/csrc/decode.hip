@@ -159,12 +159,6 @@ __global__ __launch_bounds__(64, Loop::kWaves) void decode_split(DecodeParams p)
     };
     auto compute = [&](typename Loop::Tile& t) {
         if (cc.b == 0 && cc.c == 0 && lane == 0) p.starts[cc.s] = lo + done;
-        if (done == 0 || cc.b == 0) {
-            seg_b0 = cc.b;
-            hd = stream_heads<HT>(p, cc.c);
-            L.start(st, p.q, cc.s, p.Hq, hd.head0, hd.nh);
-            vm_wait_all();  // the query loads complete on this path only
-        }
         L.block(st, t, cc.ctx - cc.b * BS, p.scale_log2);
         if (done + 1 == cnt || cc.b + 1 == cc.nb) {
             L.finish(st);
@@ -177,28 +171,38 @@ __global__ __launch_bounds__(64, Loop::kWaves) void decode_split(DecodeParams p)
         advance(cc);
         ++done;
     };
+    // Issue tile `tn`, then fold tile `tc`.  When tc opens a stream segment its
+    // queries are loaded before tn's tiles, and waited for right there, with tn's
+    // loads left in flight: the state of the previous segment is already stored.
+    auto step = [&](typename Loop::Tile& tn, typename Loop::Tile& tc) {
+        if (done == 0 || cc.b == 0) {
+            seg_b0 = cc.b;
+            hd = stream_heads<HT>(p, cc.c);
+            L.start(st, p.q, cc.s, p.Hq, hd.head0, hd.nh);
+            issue(tn);
+            vm_wait_le<Loop::kTileLoads>();
+        } else {
+            issue(tn);
+        }
+        compute(tc);
+    };
 
     if constexpr (R == 3) {  // two blocks in flight while one is folded
         issue(t0);
         issue(t1);
         while (done < cnt) {
-            issue(t2);
-            compute(t0);
+            step(t2, t0);
             if (done >= cnt) break;
-            issue(t0);
-            compute(t1);
+            step(t0, t1);
             if (done >= cnt) break;
-            issue(t1);
-            compute(t2);
+            step(t1, t2);
         }
     } else {  // one block in flight while one is folded
         issue(t0);
         while (done < cnt) {
-            issue(t1);
-            compute(t0);
+            step(t1, t0);
             if (done >= cnt) break;
-            issue(t0);
-            compute(t1);
+            step(t0, t1);
         }
     }
 }

@@ -34,6 +34,7 @@ struct MfmaLoop {
         uint4 k[KS];
         uint2 v[DT];
     };
+    static constexpr int kTileLoads = KS + DT;  // load instructions per tile
     struct State {
         float m[NH], l[NH];
         f32x4 acc[NH][DT];
@@ -211,6 +212,7 @@ struct ValuLoop {
         uint4 k[KC];
         uint4 v[VC];
     };
+    static constexpr int kTileLoads = KC + VC;  // load instructions per tile
     struct State {
         float m[GT], l[GT], acc[GT][VC];
         float q[GT][KC * VE];

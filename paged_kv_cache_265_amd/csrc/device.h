@@ -103,8 +103,14 @@ __device__ __forceinline__ uint2 stream_load8(const void* p) {
 // bytes = 0 once it has run out of tiles -- and the compiler can count exactly
 // which of its loads are still in flight.
 typedef __amdgpu_buffer_rsrc_t rsrc_t;
+// `base` and `bytes` must be wave-uniform; they are taken from the first lane so
+// that the resource sits in scalar registers.
 __device__ __forceinline__ rsrc_t tile_rsrc(const void* base, uint32_t bytes) {
-    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, (int)bytes, 0x00020000);
+    const uint64_t a = (uint64_t)base;
+    const uint64_t lo = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)a);
+    const uint64_t hi = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)(a >> 32));
+    return __builtin_amdgcn_make_buffer_rsrc((void*)(lo | (hi << 32)), 0, __builtin_amdgcn_readfirstlane((int)bytes),
+                                             0x00020000);
 }
 constexpr int kNonTemporal = 2;  // cache-policy bit of the buffer loads: nt
 __device__ __forceinline__ uint4 stream_load16(rsrc_t r, uint32_t off) {
@@ -133,6 +139,12 @@ __device__ __forceinline__ int uniform(int v) { return __builtin_amdgcn_readfirs
 // waiting for them -- and with them for everything issued before -- on every
 // path that joins afterwards.
 __device__ __forceinline__ void vm_wait_all() { __builtin_amdgcn_s_waitcnt(0x0F70); }
+// Wait until at most N vector memory accesses of this wave are outstanding
+// (vmcnt is six bits: [3:0] and [15:14] of the immediate).
+template <int N> __device__ __forceinline__ void vm_wait_le() {
+    static_assert(N >= 0 && N < 64, "vmcnt range");
+    __builtin_amdgcn_s_waitcnt(((N >> 4) << 14) | 0x0F70 | (N & 15));
+}
 
 // Scalar load of base[i] with a wave-uniform i, for tables the kernel only reads
 // (block tables, context lengths): through the constant address space the compiler
