@@ -135,8 +135,6 @@ __global__ __launch_bounds__(64, Loop::kWaves) void decode_split(DecodeParams p)
     Loop L;
     L.init_lane(lane);
     typename Loop::State st;
-    typename Loop::Tile t0, t1, t2;
-    (void)t2;
     const long long cnt = hi - lo;
     long long issued = 0, done = 0;
     Cursor ac = cur, cc = cur;
@@ -187,22 +185,15 @@ __global__ __launch_bounds__(64, Loop::kWaves) void decode_split(DecodeParams p)
         compute(tc);
     };
 
-    if constexpr (R == 3) {  // two blocks in flight while one is folded
-        issue(t0);
-        issue(t1);
-        while (done < cnt) {
-            step(t2, t0);
+    // ring of R tiles: R - 1 blocks in flight while one is folded
+    typename Loop::Tile ring[R];
+#pragma unroll
+    for (int j = 0; j + 1 < R; ++j) issue(ring[j]);
+    while (done < cnt) {
+#pragma unroll
+        for (int j = 0; j < R; ++j) {
+            step(ring[(j + R - 1) % R], ring[j]);
             if (done >= cnt) break;
-            step(t0, t1);
-            if (done >= cnt) break;
-            step(t1, t2);
-        }
-    } else {  // one block in flight while one is folded
-        issue(t0);
-        while (done < cnt) {
-            step(t1, t0);
-            if (done >= cnt) break;
-            step(t0, t1);
         }
     }
 }
@@ -232,24 +223,24 @@ __global__ __launch_bounds__(64, Loop::kWaves) void decode_fixed(DecodeParams p)
     L.init_lane(lane_id());
     typename Loop::State st;
     L.start(st, p.q, s, p.Hq, hd.head0, hd.nh);
-    // two blocks in flight while one is folded; past the end the loads are empty
-    typename Loop::Tile ta, tb, tc;
+    // ring of R tiles, R - 1 blocks in flight while one is folded; past the end
+    // the loads are empty
+    constexpr int R = Loop::kRing;
+    typename Loop::Tile ring[R];
     auto issue = [&](int i, typename Loop::Tile& t) {
         const bool live = i < nb;
         const int phys = live ? scalar_load(p.block_tables, (size_t)s * p.MB + b0 + i) : 0;
         L.load(t, p.kc, p.vc, (size_t)phys * p.Hkv + hd.kvh, live);
     };
-    issue(0, ta);
-    issue(1, tb);
-    for (int i = 0; i < nb; i += 3) {
-        issue(i + 2, tc);
-        L.block(st, ta, t1 - (b0 + i) * BS, p.scale_log2);
-        if (i + 1 >= nb) break;
-        issue(i + 3, ta);
-        L.block(st, tb, t1 - (b0 + i + 1) * BS, p.scale_log2);
-        if (i + 2 >= nb) break;
-        issue(i + 4, tb);
-        L.block(st, tc, t1 - (b0 + i + 2) * BS, p.scale_log2);
+#pragma unroll
+    for (int j = 0; j + 1 < R; ++j) issue(j, ring[j]);
+    for (int i = 0; i < nb; i += R) {
+#pragma unroll
+        for (int j = 0; j < R; ++j) {
+            issue(i + j + R - 1, ring[(j + R - 1) % R]);
+            L.block(st, ring[j], t1 - (b0 + i + j) * BS, p.scale_log2);
+            if (i + j + 1 >= nb) break;
+        }
     }
     L.finish(st);
     if (nparts == 1) {
@@ -523,10 +514,11 @@ int resident_waves(const void* f, int slot) {
     return v;
 }
 
-// tiles in the prefetch ring of the balanced split: PKV_SPLIT_DEPTH=2|3 (default 3)
-int split_depth() {
+// PKV_SPLIT_DEPTH=2 runs the balanced split with a two-tile ring (one block in
+// flight) instead of the inner loop's own depth; both pipelines stay tested
+bool shallow_split() {
     const char* e = std::getenv("PKV_SPLIT_DEPTH");
-    return (e && e[0] == '2') ? 2 : 3;
+    return e && e[0] == '2' && e[1] == 0;
 }
 
 template <class Loop, int K>
@@ -536,10 +528,9 @@ hipError_t run(const DecodeParams& p0, bool split, int slot, hipStream_t st) {
     const int NS = p.Hkv * p.chunks;
     int waves = 0;
     if (split) {
-        const int R = split_depth();
-        if (R == 3) {
-            waves = resident_waves((const void*)decode_split<Loop, 3>, slot * 2 + 1);
-            hipLaunchKernelGGL((decode_split<Loop, 3>), dim3(waves), dim3(64), 0, st, p);
+        if (!shallow_split()) {
+            waves = resident_waves((const void*)decode_split<Loop, Loop::kRing>, slot * 2 + 1);
+            hipLaunchKernelGGL((decode_split<Loop, Loop::kRing>), dim3(waves), dim3(64), 0, st, p);
         } else {
             waves = resident_waves((const void*)decode_split<Loop, 2>, slot * 2);
             hipLaunchKernelGGL((decode_split<Loop, 2>), dim3(waves), dim3(64), 0, st, p);

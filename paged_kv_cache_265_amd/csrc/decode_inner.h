@@ -27,8 +27,13 @@ struct MfmaLoop {
     static constexpr int KS = D / 32;
     static constexpr int DT = D / 16;
     static constexpr int HT = 16 * NH;
-    // waves per SIMD the register budget is sized for (two 16-head tiles need more)
-    static constexpr int kWaves = NH == 1 ? 2 : 1;
+    // Waves per SIMD the register budget is sized for, and tiles in the prefetch
+    // ring.  At head_dim 128 one wave per SIMD with a five-tile ring keeps as many
+    // bytes in flight as two waves with three tiles each, and its waves progress
+    // evenly: two waves on one SIMD share issue slots by age, so with equal work
+    // the younger one finishes far behind the older.
+    static constexpr int kWaves = (NH == 1 && D == 64) ? 2 : 1;
+    static constexpr int kRing = D == 128 ? 5 : 3;
 
     struct Tile {
         uint4 k[KS];
@@ -207,6 +212,7 @@ struct ValuLoop {
     static constexpr int VC = D * CPR / 64;            // V chunks per lane
     static constexpr int HT = GT;
     static constexpr int kWaves = ((D == 128 && (EB == 4 || GT >= 2)) || (EB == 4 && GT == 4)) ? 1 : 2;
+    static constexpr int kRing = 3;
 
     struct Tile {
         uint4 k[KC];
