@@ -257,7 +257,7 @@ def run_long(args, p, qd, qc, cu, torch, pkv, workloads, dev):
     sm = torch.from_numpy(p.token_slots[pend]).to(dev)
     out = torch.empty_like(q)
     outc = torch.empty_like(qcd)
-    ws = torch.empty(pkv.decode_workspace_size(S, 32, 1, 128, 16, p.block_tables.shape[1], 512), dtype=torch.uint8,
+    ws = torch.empty(pkv.decode_workspace_size(S, 32, 1, 128, 16, p.block_tables.shape[1], 0), dtype=torch.uint8,
                      device=dev)
     scale = 1.0 / np.sqrt(128)
     torch.cuda.synchronize()
@@ -266,7 +266,7 @@ def run_long(args, p, qd, qc, cu, torch, pkv, workloads, dev):
         pkv.reshape_and_cache(nk, nv, kc, vc, sm)
         if ev is not None:
             ev[0].record()
-        pkv.paged_attention_decode(out, q, kc, vc, bt[:S], cl[:S], scale, partition_size=512, workspace=ws)
+        pkv.paged_attention_decode(out, q, kc, vc, bt[:S], cl[:S], scale, partition_size=0, workspace=ws)
         if ev is not None:
             ev[1].record()
         pkv.paged_attention_chunked(outc, qcd, cud, 512, kc, vc, bt[S:], cl[S:], scale)
@@ -284,30 +284,30 @@ def run_long(args, p, qd, qc, cu, torch, pkv, workloads, dev):
     ms_step = (time.perf_counter() - t0) * 1e3 / args.steps
     dec_ms = float(np.mean([a.elapsed_time(b) for a, b, c in evs]))
     chk_ms = float(np.mean([b.elapsed_time(c) for a, b, c in evs]))
-    # the same decode with the library's balanced split instead of 512-token partitions
-    wsb = torch.zeros(pkv.decode_workspace_size(S, 32, 1, 128, 16, p.block_tables.shape[1], 0), dtype=torch.uint8,
-                      device=dev)
-    outb = torch.empty_like(q)
+    # the same decode with fixed 512-token partitions instead of the balanced split
+    wsf = torch.empty(pkv.decode_workspace_size(S, 32, 1, 128, 16, p.block_tables.shape[1], 512),
+                      dtype=torch.uint8, device=dev)
+    outf = torch.empty_like(q)
     for _ in range(args.warmup):
-        pkv.paged_attention_decode(outb, q, kc, vc, bt[:S], cl[:S], scale, partition_size=0, workspace=wsb)
+        pkv.paged_attention_decode(outf, q, kc, vc, bt[:S], cl[:S], scale, partition_size=512, workspace=wsf)
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     e0.record()
     for _ in range(args.steps):
-        pkv.paged_attention_decode(outb, q, kc, vc, bt[:S], cl[:S], scale, partition_size=0, workspace=wsb)
+        pkv.paged_attention_decode(outf, q, kc, vc, bt[:S], cl[:S], scale, partition_size=512, workspace=wsf)
     e1.record()
     torch.cuda.synchronize()
-    bal_ms = e0.elapsed_time(e1) / args.steps
+    fix_ms = e0.elapsed_time(e1) / args.steps
     nbytes = workloads.algorithmic_decode_bytes(p.context_lens[:S], 32, 1, 128, 2)
     flops = workloads.algorithmic_chunked_flops(p.context_lens[S:], np.diff(cu), 32, 128)
     res = {"metric": METRIC, "value": round(nbytes / (dec_ms * 1e-3) / 1e9, 1), "unit": "GB/s", "n_gpus": 1,
            "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_step, 4), "higher_is_better": True,
            "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
            "config": {"workload": "long-context mixed batch: MQA 32/1 decode of 32 seqs (context uniform "
-                                  "[16384, 131072], 512-token partitions) + 8 chunked-prefill segments of 512 "
-                                  "rows over 4096 cached tokens"},
+                                  "[16384, 131072]) + 8 chunked-prefill segments of 512 rows over 4096 cached "
+                                  "tokens"},
            "decode_ms": round(dec_ms, 4), "chunked_ms": round(chk_ms, 4),
-           "decode_balanced_split_ms": round(bal_ms, 4),
-           "decode_balanced_split_GBs": round(nbytes / (bal_ms * 1e-3) / 1e9, 1),
+           "decode_partition512_ms": round(fix_ms, 4),
+           "decode_partition512_GBs": round(nbytes / (fix_ms * 1e-3) / 1e9, 1),
            "chunked_tflops": round(flops / (chk_ms * 1e-3) / 1e12, 2),
            "roofline": {"bound": "hbm", "kernel": "paged_attention_decode", "achieved":
                         round(nbytes / (dec_ms * 1e-3) / 1e9, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
