@@ -7,12 +7,21 @@
 // attends to tokens 0 .. n - L + r (dense causal attention, "LLM 推理优化的系统视角",
 // section 3.1), through the segment's block table.
 //
-// Rows are (query token, query head of the kv group) pairs, head fastest, so
-// that the heads sharing one kv head share every K/V tile.  A workgroup of 4 waves
-// takes 128 consecutive rows; each wave owns 32 rows (two 16-row matrix-core
-// columns), walks the key blocks 0 .. (its last position)/16, and keeps an online
-// softmax per row.  Scores S^T = K Q^T use 16x16x32 matrix cores, P V uses
-// 16x16x16 matrix cores with P split into high and low 16-bit parts.
+// Rows are (query token, query head of the kv group) pairs, head fastest, so that
+// the heads sharing one kv head share every K/V tile.  A workgroup of 4 waves takes
+// 128 consecutive rows of one (segment, kv head); each wave owns 32 of them (two
+// 16-row matrix-core columns).  The keys go by in steps of 32 (two pool blocks):
+// the workgroup stages a step's K and V into LDS once, double-buffered, and every
+// wave folds it into its rows with an online softmax:
+//   S^T = K Q^T        16x16x32 matrix cores, 16 keys x 16 rows per product
+//   O^T += V^T P^T     16x16x32 matrix cores over all 32 keys of the step, P split
+//                      into high and low 16-bit parts so that it keeps fp32 accuracy
+// LDS layouts (rows padded by 16 bytes, so that the 16 lanes reading one 16-byte
+// column hit 16 distinct bank quads):
+//   K: [32 keys][D] as in the pool tile
+//   V: [D][4 groups][8]: group g holds keys 4g..4g+3 of the first block, then keys
+//      4g..4g+3 of the second -- exactly the 8 keys whose probabilities lane group g
+//      holds after the score product, so one 16-byte read is one matrix-core operand.
 #include "device.h"
 #include "internal.h"
 
@@ -20,16 +29,30 @@ namespace pkv {
 
 namespace {
 
-constexpr int NW = 4;
+constexpr int NW = 4;                  // waves per workgroup
 constexpr int BS = kBlockSize;
 constexpr int ROWS_PER_WAVE = 32;
 constexpr int ROWS_PER_WG = NW * ROWS_PER_WAVE;
+constexpr int NH = ROWS_PER_WAVE / 16;  // 16-row tiles per wave
+constexpr int KSTEP = 2 * BS;          // keys per step
+
+template <int D>
+struct ChunkLds {
+    static constexpr int KROW = D * 2 + 16;      // bytes per key row of K
+    static constexpr int VROW = 4 * 16 + 16;     // bytes per head_dim row of V
+    static constexpr int KBYTES = KSTEP * KROW;
+    static constexpr int VBYTES = D * VROW;
+    static constexpr int STAGE = KBYTES + VBYTES;
+    static constexpr int CHUNKS = KSTEP * D * 2 / 16 / (NW * 64);  // 16-byte K (and V) pieces per thread
+};
 
 template <int K, int D>
-__global__ __launch_bounds__(NW * 64) void chunked_mfma(ChunkedParams p) {
+__global__ __launch_bounds__(NW * 64, 2) void chunked_fa(ChunkedParams p) {
     constexpr int KS = D / 32;
     constexpr int DT = D / 16;
-    constexpr int NH = ROWS_PER_WAVE / 16;
+    using Lds = ChunkLds<D>;
+    constexpr uint32_t kTile = BS * D * 2;  // bytes of one (block, kv head) tile
+    __shared__ __attribute__((aligned(16))) char lds[2 * Lds::STAGE];
 
     const int G = p.G;
     const int tiles = (p.max_q_len * G + ROWS_PER_WG - 1) / ROWS_PER_WG;
@@ -43,36 +66,41 @@ __global__ __launch_bounds__(NW * 64) void chunked_mfma(ChunkedParams p) {
     const int L = p.cu_q_lens[seg + 1] - qb0;
     const int n = p.context_lens[seg];
     const int nrows = L * G;
-    const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-    const int row0 = tile * ROWS_PER_WG + w * ROWS_PER_WAVE;
-    if (row0 >= nrows) return;  // whole wave idle (no barriers in this kernel)
+    const int wg_row0 = tile * ROWS_PER_WG;
+    if (wg_row0 >= nrows) return;  // whole workgroup idle, before any barrier
+    const int nblk = (n + BS - 1) / BS;
+    // keys the workgroup needs: 0 .. position of its last live row
+    const int wg_last = min(wg_row0 + ROWS_PER_WG, nrows) - 1;
+    const int nsteps = (n - L + wg_last / G) / KSTEP + 1;
 
+    const int tid = threadIdx.x;
+    const int w = uniform(tid >> 6);
     const int lane = lane_id();
     const int col = lane & 15;
     const int gq = lane >> 4;
+    const int row0 = wg_row0 + w * ROWS_PER_WAVE;
+    const bool wave_live = row0 < nrows;
+    // positions of the wave's first and last live rows (rows are sorted by position)
+    const int wave_first_pos = n - L + row0 / G;
+    const int wave_last_pos = n - L + (min(row0 + ROWS_PER_WAVE, nrows) - 1) / G;
 
-    // rows of this lane's two columns
+    // this lane's rows: Q as the B operand of the score product; dead rows see
+    // every key with a zero query (finite, never stored)
     int pos[NH];
-    bool live[NH];
-    uint4 qb[NH][KS];
+    uint4 qv[NH][KS];
     const uint16_t* qp = (const uint16_t*)p.q;
 #pragma unroll
     for (int ht = 0; ht < NH; ++ht) {
         const int r = row0 + ht * 16 + col;
-        live[ht] = r < nrows;
-        const int tok = live[ht] ? r / G : 0;
-        const int j = live[ht] ? r - tok * G : 0;
-        pos[ht] = live[ht] ? n - L + tok : 0;
+        const bool live = r < nrows;
+        const int tok = live ? r / G : 0;
+        const int j = live ? r - tok * G : 0;
+        pos[ht] = live ? n - L + tok : n - 1;
 #pragma unroll
         for (int ks = 0; ks < KS; ++ks)
-            qb[ht][ks] = live[ht] ? *(const uint4*)(qp + ((size_t)(qb0 + tok) * p.Hq + kvh * G + j) * D +
-                                                    (gq + 4 * ks) * 8)
-                                  : make_uint4(0, 0, 0, 0);
+            qv[ht][ks] = live ? *(const uint4*)(qp + ((size_t)(qb0 + tok) * p.Hq + kvh * G + j) * D + (gq + 4 * ks) * 8)
+                              : make_uint4(0, 0, 0, 0);
     }
-    const int last_row = min(row0 + ROWS_PER_WAVE, nrows) - 1;
-    const int last_pos = n - L + last_row / G;
-    const int nkb = last_pos / BS + 1;
-
     float m[NH], l[NH];
     f32x4 acc[NH][DT];
 #pragma unroll
@@ -83,91 +111,170 @@ __global__ __launch_bounds__(NW * 64) void chunked_mfma(ChunkedParams p) {
         for (int dt = 0; dt < DT; ++dt) acc[ht][dt] = f32x4{0.f, 0.f, 0.f, 0.f};
     }
 
-    const uint16_t* kc = (const uint16_t*)p.kc;
-    const uint16_t* vc = (const uint16_t*)p.vc;
+    // ---- staging: this thread's 16-byte pieces of K and V for one step -------------
     const int32_t* table = p.block_tables + (size_t)seg * p.MB;
-    const size_t tsz = (size_t)BS * D;
-    int koff[KS], voff[DT];
+    struct Staged {
+        uint4 k[Lds::CHUNKS], v[Lds::CHUNKS];
+    };
+    // loads of blocks past the context are empty (zero bytes, no memory access), so
+    // every step issues the same loads and the wait before staging counts exactly
+    auto fetch = [&](int step, Staged& r) {
+        const int b0 = step * 2;
+        const bool live0 = b0 < nblk, live1 = b0 + 1 < nblk;
+        const int ph0 = live0 ? scalar_load(table, (size_t)uniform(b0)) : 0;
+        const int ph1 = live1 ? scalar_load(table, (size_t)uniform(b0 + 1)) : 0;
+        const size_t t0 = ((size_t)ph0 * p.Hkv + kvh) * kTile, t1 = ((size_t)ph1 * p.Hkv + kvh) * kTile;
+        const rsrc_t k0 = tile_rsrc((const char*)p.kc + t0, live0 ? kTile : 0);
+        const rsrc_t k1 = tile_rsrc((const char*)p.kc + t1, live1 ? kTile : 0);
+        const rsrc_t v0 = tile_rsrc((const char*)p.vc + t0, live0 ? kTile : 0);
+        const rsrc_t v1 = tile_rsrc((const char*)p.vc + t1, live1 ? kTile : 0);
 #pragma unroll
-    for (int ks = 0; ks < KS; ++ks) koff[ks] = col * D + (gq + 4 * ks) * 8;
+        for (int i = 0; i < Lds::CHUNKS; ++i) {
+            const int c = tid + i * NW * 64;                // piece of the step: block c / (kTile/16)
+            const uint32_t off = (uint32_t)(c % (kTile / 16)) * 16;
+            const bool second = c >= (int)(kTile / 16);
+            r.k[i] = second ? stream_load16(k1, off) : stream_load16(k0, off);
+            r.v[i] = second ? stream_load16(v1, off) : stream_load16(v0, off);
+        }
+    };
+    auto stage = [&](int step, const Staged& r, int buf) {
+        char* kl = lds + buf * Lds::STAGE;
+        char* vl = kl + Lds::KBYTES;
 #pragma unroll
-    for (int dt = 0; dt < DT; ++dt) voff[dt] = (dt * 16 + col) * BS + 4 * gq;
+        for (int i = 0; i < Lds::CHUNKS; ++i) {
+            const int c = tid + i * NW * 64;
+            const int blk = c / (int)(kTile / 16);
+            const int off = (c % (int)(kTile / 16)) * 16;
+            // K: key row (within the step), 16-byte column
+            const int key = blk * BS + off / (D * 2);
+            *(uint4*)(kl + key * Lds::KROW + off % (D * 2)) = r.k[i];
+            // V: head_dim row d, tokens 8h .. 8h+7 of block blk; slots past the
+            // context may hold anything and are zeroed
+            const int d = off / (BS * 2);
+            const int h = (off % (BS * 2)) / 16;
+            uint4 v = r.v[i];
+            const int tok0 = step * KSTEP + blk * BS + 8 * h;
+            if (tok0 + 8 > n) {
+                uint32_t u[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+                for (int e = 0; e < 8; ++e)
+                    if (tok0 + e >= n) u[e / 2] &= (e & 1) ? 0x0000ffffu : 0xffff0000u;
+                v = make_uint4(u[0], u[1], u[2], u[3]);
+            }
+            char* vr = vl + d * Lds::VROW + blk * 8;
+            *(uint2*)(vr + (2 * h) * 16) = make_uint2(v.x, v.y);
+            *(uint2*)(vr + (2 * h + 1) * 16) = make_uint2(v.z, v.w);
+        }
+    };
 
-    struct Tile {
-        uint4 k[KS];
-        uint2 v[DT];
-    };
-    auto load = [&](int kb, Tile& t) {
-        const int phys = table[kb];
-        const size_t base = ((size_t)phys * p.Hkv + kvh) * tsz;
+    // ---- one step: 32 keys into this wave's 32 rows ----------------------------------
+    auto fold = [&](int step, int buf) {
+        const char* kl = lds + buf * Lds::STAGE;
+        const char* vl = kl + Lds::KBYTES;
+        const int key0 = step * KSTEP;
+        // four independent score chains (2 key halves x 2 row tiles) per k-step, so
+        // consecutive matrix-core products never wait on each other
+        uint4 kf[2][KS];
 #pragma unroll
-        for (int ks = 0; ks < KS; ++ks) t.k[ks] = *(const uint4*)(kc + base + koff[ks]);
+        for (int kh = 0; kh < 2; ++kh)
 #pragma unroll
-        for (int dt = 0; dt < DT; ++dt) t.v[dt] = *(const uint2*)(vc + base + voff[dt]);
-    };
-    auto compute = [&](int kb, Tile& t) {
-        const int key0 = kb * BS + 4 * gq;  // keys of this lane's four score rows
-        uint2 phi[NH], plo[NH];
+            for (int ks = 0; ks < KS; ++ks)
+                kf[kh][ks] = *(const uint4*)(kl + (kh * BS + col) * Lds::KROW + (gq + 4 * ks) * 16);
+        f32x4 sc[2][NH];
+#pragma unroll
+        for (int kh = 0; kh < 2; ++kh)
+#pragma unroll
+            for (int ht = 0; ht < NH; ++ht) sc[kh][ht] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks)
+#pragma unroll
+            for (int kh = 0; kh < 2; ++kh)
+#pragma unroll
+                for (int ht = 0; ht < NH; ++ht) sc[kh][ht] = mma_16x16x32<K>(kf[kh][ks], qv[ht][ks], sc[kh][ht]);
+        // V fragments, read while the softmax runs
+        uint4 vf[DT];
+#pragma unroll
+        for (int dt = 0; dt < DT; ++dt) vf[dt] = *(const uint4*)(vl + (dt * 16 + col) * Lds::VROW + gq * 16);
+        // keys of this lane's eight scores: key0 + 4 gq + j and key0 + 16 + 4 gq + j
+        const bool masked = key0 + KSTEP - 1 > wave_first_pos;
+        uint4 phi[NH], plo[NH];
 #pragma unroll
         for (int ht = 0; ht < NH; ++ht) {
-            f32x4 sc = {0.f, 0.f, 0.f, 0.f};
+            float s[8];
 #pragma unroll
-            for (int ks = 0; ks < KS; ++ks) sc = mma_16x16x32<K>(t.k[ks], qb[ht][ks], sc);
-            float sv[4];
+            for (int j = 0; j < 4; ++j) {
+                s[j] = sc[0][ht][j] * p.scale_log2;
+                s[4 + j] = sc[1][ht][j] * p.scale_log2;
+            }
+            if (masked) {
 #pragma unroll
-            for (int j = 0; j < 4; ++j) sv[j] = (key0 + j <= pos[ht]) ? sc[j] * p.scale_log2 : kNegInf;
-            float bm = fmaxf(fmaxf(sv[0], sv[1]), fmaxf(sv[2], sv[3]));
+                for (int j = 0; j < 4; ++j) {
+                    if (key0 + 4 * gq + j > pos[ht]) s[j] = kNegInf;
+                    if (key0 + BS + 4 * gq + j > pos[ht]) s[4 + j] = kNegInf;
+                }
+            }
+            float bm = fmaxf(fmaxf(fmaxf(s[0], s[1]), fmaxf(s[2], s[3])), fmaxf(fmaxf(s[4], s[5]), fmaxf(s[6], s[7])));
             bm = xor_max(bm, 16);
             bm = xor_max(bm, 32);
-            // key 0 is visible to every row, so m is finite from the first block on
+            // key 0 is visible to every row, so m is finite from the first step on
             const float mn = fmaxf(m[ht], bm);
             const float alpha = fast_exp2(m[ht] - mn);
-            float pr[4];
+            float pr[8];
 #pragma unroll
-            for (int j = 0; j < 4; ++j) pr[j] = fast_exp2(sv[j] - mn);
-            l[ht] = l[ht] * alpha + ((pr[0] + pr[1]) + (pr[2] + pr[3]));
+            for (int j = 0; j < 8; ++j) pr[j] = fast_exp2(s[j] - mn);
+            l[ht] = l[ht] * alpha + (((pr[0] + pr[1]) + (pr[2] + pr[3])) + ((pr[4] + pr[5]) + (pr[6] + pr[7])));
+            if (__ballot(mn != m[ht])) {  // alpha = 1 in every lane otherwise
+#pragma unroll
+                for (int dt = 0; dt < DT; ++dt) acc[ht][dt] *= alpha;
+            }
             m[ht] = mn;
-#pragma unroll
-            for (int dt = 0; dt < DT; ++dt) acc[ht][dt] *= alpha;
-            phi[ht] = pack4<K>(pr[0], pr[1], pr[2], pr[3]);
-            plo[ht] = pack4<K>(pr[0] - lo16<K>(phi[ht].x), pr[1] - hi16<K>(phi[ht].x), pr[2] - lo16<K>(phi[ht].y),
-                               pr[3] - hi16<K>(phi[ht].y));
+            const uint2 h0 = pack4<K>(pr[0], pr[1], pr[2], pr[3]);
+            const uint2 h1 = pack4<K>(pr[4], pr[5], pr[6], pr[7]);
+            const uint2 l0 = pack4<K>(pr[0] - lo16<K>(h0.x), pr[1] - hi16<K>(h0.x), pr[2] - lo16<K>(h0.y),
+                                      pr[3] - hi16<K>(h0.y));
+            const uint2 l1 = pack4<K>(pr[4] - lo16<K>(h1.x), pr[5] - hi16<K>(h1.x), pr[6] - lo16<K>(h1.y),
+                                      pr[7] - hi16<K>(h1.y));
+            phi[ht] = make_uint4(h0.x, h0.y, h1.x, h1.y);
+            plo[ht] = make_uint4(l0.x, l0.y, l1.x, l1.y);
         }
-        if (kb * BS + BS > n) {  // slots past the context may hold anything (NaN)
+        // high parts first, then the remainders: an accumulator is reused only
+        // 2 * DT products later
 #pragma unroll
-            for (int dt = 0; dt < DT; ++dt) {
-                uint32_t x = t.v[dt].x, y = t.v[dt].y;
-                if (key0 + 0 >= n) x &= 0xffff0000u;
-                if (key0 + 1 >= n) x &= 0x0000ffffu;
-                if (key0 + 2 >= n) y &= 0xffff0000u;
-                if (key0 + 3 >= n) y &= 0x0000ffffu;
-                t.v[dt] = make_uint2(x, y);
-            }
-        }
+        for (int dt = 0; dt < DT; ++dt)
 #pragma unroll
-        for (int dt = 0; dt < DT; ++dt) {
+            for (int ht = 0; ht < NH; ++ht) acc[ht][dt] = mma_16x16x32<K>(vf[dt], phi[ht], acc[ht][dt]);
 #pragma unroll
-            for (int ht = 0; ht < NH; ++ht) {
-                acc[ht][dt] = mma_16x16x16<K>(t.v[dt], phi[ht], acc[ht][dt]);
-                acc[ht][dt] = mma_16x16x16<K>(t.v[dt], plo[ht], acc[ht][dt]);
-            }
-        }
+        for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+            for (int ht = 0; ht < NH; ++ht) acc[ht][dt] = mma_16x16x32<K>(vf[dt], plo[ht], acc[ht][dt]);
     };
 
-    Tile ta, tb;
-    load(0, ta);
-    for (int kb = 0; kb < nkb; kb += 2) {
-        if (kb + 1 < nkb) load(kb + 1, tb);
-        compute(kb, ta);
-        if (kb + 2 < nkb) load(kb + 2, ta);
-        if (kb + 1 < nkb) compute(kb + 1, tb);
+    // step s lives in LDS buffer s % 2; its loads were issued two steps earlier
+    // into register set s % 2
+    Staged r0, r1;
+    fetch(0, r0);
+    fetch(1, r1);
+    stage(0, r0, 0);
+    __syncthreads();
+    for (int step = 0; step < nsteps; step += 2) {
+        fetch(step + 2, r0);
+        // a wave whose rows all lie before this step's first key has nothing to fold
+        if (wave_live && step * KSTEP <= wave_last_pos) fold(step, 0);
+        stage(step + 1, r1, 1);
+        __syncthreads();
+        if (step + 1 >= nsteps) break;
+        fetch(step + 3, r1);
+        if (wave_live && (step + 1) * KSTEP <= wave_last_pos) fold(step + 1, 1);
+        stage(step + 2, r0, 0);
+        __syncthreads();
     }
+    if (!wave_live) return;
 
 #pragma unroll
     for (int ht = 0; ht < NH; ++ht) {
         l[ht] = xor_sum(xor_sum(l[ht], 16), 32);
-        if (!live[ht]) continue;
         const int r = row0 + ht * 16 + col;
+        if (r >= nrows) continue;
         const int tok = r / G;
         const int j = r - tok * G;
         const float inv = 1.f / l[ht];
@@ -185,7 +292,7 @@ hipError_t run(const ChunkedParams& p, hipStream_t st) {
     const long long tiles = ((long long)p.max_q_len * p.G + ROWS_PER_WG - 1) / ROWS_PER_WG;
     const long long grid = tiles * p.Hkv * p.num_segs;
     if (grid == 0) return hipSuccess;
-    hipLaunchKernelGGL((chunked_mfma<K, D>), dim3((unsigned)grid), dim3(NW * 64), 0, st, p);
+    hipLaunchKernelGGL((chunked_fa<K, D>), dim3((unsigned)grid), dim3(NW * 64), 0, st, p);
     return hipGetLastError();
 }
 

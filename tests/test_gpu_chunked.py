@@ -45,6 +45,8 @@ CASES = [
     ("f16", 8, 1, 128, [0], [130]),
     ("bf16", 3, 2, 64, [10, 77, 0], [5, 9, 20]),
     ("bf16", 40, 1, 64, [33], [6]),
+    ("bf16", 4, 2, 128, [1000, 37], [200, 95]),   # many 32-key steps, odd block counts
+    ("f16", 32, 1, 64, [513], [77]),
 ]
 
 
