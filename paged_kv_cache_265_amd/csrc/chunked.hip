@@ -130,11 +130,12 @@ __global__ __launch_bounds__(NW * 64, 2) void chunked_fa(ChunkedParams p) {
         const rsrc_t v1 = tile_rsrc((const char*)p.vc + t1, live1 ? kTile : 0);
 #pragma unroll
         for (int i = 0; i < Lds::CHUNKS; ++i) {
-            const int c = tid + i * NW * 64;                // piece of the step: block c / (kTile/16)
+            const int c = tid + i * NW * 64;  // piece c of the step lies in block c / (kTile/16)
             const uint32_t off = (uint32_t)(c % (kTile / 16)) * 16;
-            const bool second = c >= (int)(kTile / 16);
-            r.k[i] = second ? stream_load16(k1, off) : stream_load16(k0, off);
-            r.v[i] = second ? stream_load16(v1, off) : stream_load16(v0, off);
+            // a wave's 64 pieces never straddle the two blocks (kTile/16 is a multiple of 64)
+            const bool second = uniform(c / (int)(kTile / 16)) != 0;
+            r.k[i] = stream_load16(second ? k1 : k0, off);
+            r.v[i] = stream_load16(second ? v1 : v0, off);
         }
     };
     auto stage = [&](int step, const Staged& r, int buf) {
@@ -197,14 +198,17 @@ __global__ __launch_bounds__(NW * 64, 2) void chunked_fa(ChunkedParams p) {
         for (int dt = 0; dt < DT; ++dt) vf[dt] = *(const uint4*)(vl + (dt * 16 + col) * Lds::VROW + gq * 16);
         // keys of this lane's eight scores: key0 + 4 gq + j and key0 + 16 + 4 gq + j
         const bool masked = key0 + KSTEP - 1 > wave_first_pos;
+        // the running max m is kept on unscaled scores (scale > 0 keeps the order);
+        // p = 2^(c s - c m) is one fused multiply-add and one exp2 per score
+        const float c = p.scale_log2;
         uint4 phi[NH], plo[NH];
 #pragma unroll
         for (int ht = 0; ht < NH; ++ht) {
             float s[8];
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
-                s[j] = sc[0][ht][j] * p.scale_log2;
-                s[4 + j] = sc[1][ht][j] * p.scale_log2;
+                s[j] = sc[0][ht][j];
+                s[4 + j] = sc[1][ht][j];
             }
             if (masked) {
 #pragma unroll
@@ -218,10 +222,11 @@ __global__ __launch_bounds__(NW * 64, 2) void chunked_fa(ChunkedParams p) {
             bm = xor_max(bm, 32);
             // key 0 is visible to every row, so m is finite from the first step on
             const float mn = fmaxf(m[ht], bm);
-            const float alpha = fast_exp2(m[ht] - mn);
+            const float alpha = fast_exp2((m[ht] - mn) * c);
+            const float off = -mn * c;
             float pr[8];
 #pragma unroll
-            for (int j = 0; j < 8; ++j) pr[j] = fast_exp2(s[j] - mn);
+            for (int j = 0; j < 8; ++j) pr[j] = fast_exp2(__builtin_fmaf(s[j], c, off));
             l[ht] = l[ht] * alpha + (((pr[0] + pr[1]) + (pr[2] + pr[3])) + ((pr[4] + pr[5]) + (pr[6] + pr[7])));
             if (__ballot(mn != m[ht])) {  // alpha = 1 in every lane otherwise
 #pragma unroll

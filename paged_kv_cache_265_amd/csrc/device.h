@@ -54,12 +54,21 @@ template <int K> __device__ __forceinline__ void store_elem(void* base, size_t i
         ((uint16_t*)base)[i] = to_bits16<K>(x);
 }
 
+// Two fp32 values -> two 16-bit values in one word (a in the low half), round to
+// nearest even: one two-source conversion instruction on gfx950.
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+template <int K> __device__ __forceinline__ uint32_t pack2(float a, float b);
+template <> __device__ __forceinline__ uint32_t pack2<KBF16>(float a, float b) {
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2){a, b}, bf16x2));
+}
+template <> __device__ __forceinline__ uint32_t pack2<KF16>(float a, float b) {
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2){a, b}, f16x2));
+}
+
 // Four fp32 values -> four 16-bit values packed in 8 bytes.
 template <int K> __device__ __forceinline__ uint2 pack4(float a, float b, float c, float d) {
-    uint2 r;
-    r.x = (uint32_t)to_bits16<K>(a) | ((uint32_t)to_bits16<K>(b) << 16);
-    r.y = (uint32_t)to_bits16<K>(c) | ((uint32_t)to_bits16<K>(d) << 16);
-    return r;
+    return make_uint2(pack2<K>(a, b), pack2<K>(c, d));
 }
 
 // ---- matrix cores --------------------------------------------------------------------
