@@ -198,8 +198,6 @@ __global__ __launch_bounds__(NW * 64, 2) void chunked_fa(ChunkedParams p) {
         for (int dt = 0; dt < DT; ++dt) vf[dt] = *(const uint4*)(vl + (dt * 16 + col) * Lds::VROW + gq * 16);
         // keys of this lane's eight scores: key0 + 4 gq + j and key0 + 16 + 4 gq + j
         const bool masked = key0 + KSTEP - 1 > wave_first_pos;
-        // the running max m is kept on unscaled scores (scale > 0 keeps the order);
-        // p = 2^(c s - c m) is one fused multiply-add and one exp2 per score
         const float c = p.scale_log2;
         uint4 phi[NH], plo[NH];
 #pragma unroll
@@ -220,19 +218,21 @@ __global__ __launch_bounds__(NW * 64, 2) void chunked_fa(ChunkedParams p) {
             float bm = fmaxf(fmaxf(fmaxf(s[0], s[1]), fmaxf(s[2], s[3])), fmaxf(fmaxf(s[4], s[5]), fmaxf(s[6], s[7])));
             bm = xor_max(bm, 16);
             bm = xor_max(bm, 32);
+            bm *= c;  // the scale is positive: the max of the scaled scores
             // key 0 is visible to every row, so m is finite from the first step on
-            const float mn = fmaxf(m[ht], bm);
-            const float alpha = fast_exp2((m[ht] - mn) * c);
-            const float off = -mn * c;
+            if (__ballot(bm > m[ht] + kRescaleSlack)) {
+                const float mn = fmaxf(m[ht], bm);
+                const float alpha = fast_exp2(m[ht] - mn);
+                l[ht] *= alpha;
+#pragma unroll
+                for (int dt = 0; dt < DT; ++dt) acc[ht][dt] *= alpha;
+                m[ht] = mn;
+            }
+            const float off = -m[ht];
             float pr[8];
 #pragma unroll
             for (int j = 0; j < 8; ++j) pr[j] = fast_exp2(__builtin_fmaf(s[j], c, off));
-            l[ht] = l[ht] * alpha + (((pr[0] + pr[1]) + (pr[2] + pr[3])) + ((pr[4] + pr[5]) + (pr[6] + pr[7])));
-            if (__ballot(mn != m[ht])) {  // alpha = 1 in every lane otherwise
-#pragma unroll
-                for (int dt = 0; dt < DT; ++dt) acc[ht][dt] *= alpha;
-            }
-            m[ht] = mn;
+            l[ht] += ((pr[0] + pr[1]) + (pr[2] + pr[3])) + ((pr[4] + pr[5]) + (pr[6] + pr[7]));
             const uint2 h0 = pack4<K>(pr[0], pr[1], pr[2], pr[3]);
             const uint2 h1 = pack4<K>(pr[4], pr[5], pr[6], pr[7]);
             const uint2 l0 = pack4<K>(pr[0] - lo16<K>(h0.x), pr[1] - hi16<K>(h0.x), pr[2] - lo16<K>(h0.y),

@@ -97,22 +97,29 @@ struct MfmaLoop {
             for (int ks = 0; ks < KS; ++ks) sc = mma_16x16x32<K>(t.k[ks], st.q[ht][ks], sc);
             float sv[4];
 #pragma unroll
-            for (int j = 0; j < 4; ++j) sv[j] = (4 * gq + j < valid) ? sc[j] * scale_log2 : kNegInf;
+            for (int j = 0; j < 4; ++j) sv[j] = sc[j];
+            if (valid < kBlockSize) {
+#pragma unroll
+                for (int j = 0; j < 4; ++j)
+                    if (4 * gq + j >= valid) sv[j] = kNegInf;
+            }
             float bm = fmaxf(fmaxf(sv[0], sv[1]), fmaxf(sv[2], sv[3]));
             bm = xor_max(bm, 16);
             bm = xor_max(bm, 32);
-            const float mn = fmaxf(st.m[ht], bm);
-            const float alpha = fast_exp2(st.m[ht] - mn);
-            float pr[4];
-#pragma unroll
-            for (int j = 0; j < 4; ++j) pr[j] = fast_exp2(sv[j] - mn);
-            st.l[ht] = st.l[ht] * alpha + ((pr[0] + pr[1]) + (pr[2] + pr[3]));
-            // rescaling by alpha = 1 changes nothing: skip it when no lane's max moved
-            if (__ballot(mn != st.m[ht])) {
+            bm *= scale_log2;  // the scale is positive: the max of the scaled scores
+            if (__ballot(bm > st.m[ht] + kRescaleSlack)) {
+                const float mn = fmaxf(st.m[ht], bm);
+                const float alpha = fast_exp2(st.m[ht] - mn);
+                st.l[ht] *= alpha;
 #pragma unroll
                 for (int dt = 0; dt < DT; ++dt) st.acc[ht][dt] *= alpha;
+                st.m[ht] = mn;
             }
-            st.m[ht] = mn;
+            const float off = -st.m[ht];
+            float pr[4];
+#pragma unroll
+            for (int j = 0; j < 4; ++j) pr[j] = fast_exp2(__builtin_fmaf(sv[j], scale_log2, off));
+            st.l[ht] += (pr[0] + pr[1]) + (pr[2] + pr[3]);
             phi[ht] = pack4<K>(pr[0], pr[1], pr[2], pr[3]);
             plo[ht] = pack4<K>(pr[0] - lo16<K>(phi[ht].x), pr[1] - hi16<K>(phi[ht].x), pr[2] - lo16<K>(phi[ht].y),
                                pr[3] - hi16<K>(phi[ht].y));
@@ -282,15 +289,16 @@ struct ValuLoop {
             bm = xor_max(bm, 8);
             bm = xor_max(bm, 16);
             bm = xor_max(bm, 32);
-            const float mn = fmaxf(st.m[j], bm);
-            const float alpha = fast_exp2(st.m[j] - mn);
-            pj[j] = fast_exp2(sv - mn);
-            st.l[j] = st.l[j] * alpha + (sub == 0 ? pj[j] : 0.f);
-            if (__ballot(mn != st.m[j])) {  // alpha = 1 everywhere otherwise
+            if (__ballot(bm > st.m[j] + kRescaleSlack)) {  // bm is the same in every lane
+                const float mn = fmaxf(st.m[j], bm);
+                const float alpha = fast_exp2(st.m[j] - mn);
+                st.l[j] *= alpha;
 #pragma unroll
                 for (int c = 0; c < VC; ++c) st.acc[j][c] *= alpha;
+                st.m[j] = mn;
             }
-            st.m[j] = mn;
+            pj[j] = fast_exp2(sv - st.m[j]);
+            st.l[j] += sub == 0 ? pj[j] : 0.f;
         }
         float vf[VC][VE];
 #pragma unroll

@@ -172,6 +172,12 @@ __device__ __forceinline__ float xor_max(float v, int mask) { return fmaxf(v, __
 __device__ __forceinline__ float xor_sum(float v, int mask) { return v + __shfl_xor(v, mask, 64); }
 
 constexpr float kLog2e = 1.4426950408889634f;
+// Online softmax with a lazy reference: probabilities are 2^(x - m) with x the
+// scaled score and m a reference that is raised (and the running sums rescaled)
+// only when some row's maximum exceeds it by more than this many powers of two.
+// In between, probabilities stay below 2^8 -- far inside fp32 (and 16-bit) range
+// -- and the common case skips the rescale entirely.
+constexpr float kRescaleSlack = 8.f;
 constexpr float kNegInf = -__builtin_huge_valf();
 
 }  // namespace pkv
