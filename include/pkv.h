@@ -85,15 +85,23 @@ enum pkv_status {
 int pkv_version(void);
 
 /* Partition length (tokens) that paged_attention_decode uses for the given
- * arguments: partition_size itself when > 0, else the library's choice (a
- * multiple of block_size that depends only on these host scalars).  Returns a
- * negative status on invalid arguments. */
+ * arguments: partition_size itself when > 0; 0 when partition_size is 0, meaning
+ * the balanced split (see paged_attention_decode).  Returns a negative status
+ * when block_size <= 0 or partition_size is negative or not a multiple of
+ * block_size. */
 int pkv_decode_partition_size(int num_seqs, int num_q_heads, int num_kv_heads, int head_dim, int block_size,
                               int max_blocks_per_seq, int partition_size);
 
-/* Bytes of workspace paged_attention_decode needs.  Zero when every sequence fits
- * one partition (max_blocks_per_seq * block_size <= partition length).  Returns 0
- * on invalid arguments as well; the decode call then reports the error. */
+/* Bytes of workspace paged_attention_decode needs.
+ *   partition_size == 0 (balanced split): a fixed amount that depends on num_seqs,
+ *     the heads per kv head and head_dim only -- an int64 per sequence plus room
+ *     for two fp32 records of (head_dim + 2) values per query head of a kv head
+ *     for each of at most 8192 waves (about 34 MB at 4 query heads per kv head,
+ *     head_dim 128).
+ *   partition_size > 0: one such record per (sequence, query head, partition);
+ *     zero when every sequence fits one partition (max_blocks_per_seq *
+ *     block_size <= partition_size).
+ * Returns 0 on invalid arguments as well; the decode call then reports the error. */
 size_t pkv_decode_workspace_size(int num_seqs, int num_q_heads, int num_kv_heads, int head_dim, int block_size,
                                  int max_blocks_per_seq, int partition_size);
 
@@ -107,13 +115,21 @@ size_t pkv_decode_workspace_size(int num_seqs, int num_q_heads, int num_kv_heads
  *   x_t = scale * (query[s][h][:] . K_t).
  * The softmax is one softmax over all n tokens.  n = 0 gives a zero output.
  *
- * Long contexts are split into partitions of pkv_decode_partition_size() tokens;
- * each partition keeps (running max, running sum, unnormalised output) in the
- * workspace and a second kernel merges them.
+ * The work is cut into pieces, each keeping (reference max, sum, unnormalised
+ * output) in the workspace; a second kernel merges the pieces of every cut
+ * sequence ([P3] section 4.2: tiling changes the order of the sums, not the
+ * result):
+ *   partition_size == 0: balanced split -- the (sequence, kv head, 16-token
+ *     block) units of the whole batch are dealt out in equal contiguous ranges to
+ *     as many one-wave workgroups as the GPU holds at once.
+ *   partition_size > 0: fixed partitions of that many tokens per sequence.
  *   workspace / workspace_bytes: device buffer of at least
- *   pkv_decode_workspace_size(...) bytes (may be NULL when that size is 0).  Its
- *   contents on entry do not matter and are undefined on return.
- *   partition_size: 0 = library choice, else a positive multiple of block_size.
+ *   pkv_decode_workspace_size(...) bytes, 16-byte aligned (may be NULL when that
+ *   size is 0).  Its contents on entry do not matter and are undefined on
+ *   return.  Calls that share a workspace must not overlap in time.
+ *   partition_size: 0 or a positive multiple of block_size.
+ * Results do not depend on partition_size beyond fp32 rounding order, and a
+ * given call is deterministic (bit for bit on repeat).
  */
 int paged_attention_decode(void* out, const void* query, const void* key_cache, const void* value_cache,
                            const int32_t* block_tables, const int32_t* context_lens, int num_seqs,
