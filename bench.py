@@ -113,6 +113,42 @@ def cpu_baseline(case, budget_s: float = 10.0):
             "seqs_per_s": round(case.num_seqs * runs / spent, 1)}
 
 
+def cold_calls(torch, pkv, dev, call, n: int = 20):
+    """Times of `call` with the 256 MB last-level cache evicted before each one (a
+    512 MiB write outside the timed events)."""
+    scratch = torch.empty(512 << 20, dtype=torch.uint8, device=dev)
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(n)]
+    for i in range(n):
+        scratch.fill_(i & 255)
+        evs[i][0].record()
+        call()
+        evs[i][1].record()
+    torch.cuda.synchronize()
+    del scratch
+    torch.cuda.empty_cache()
+    return np.array([a.elapsed_time(b) for a, b in evs])
+
+
+def read_ceiling(torch, pkv, dev, nbytes: int = 4 << 30) -> float:
+    """GB/s of pkv_read_probe over a 4 GiB buffer: the decode kernels' load shape
+    with nothing else to do, a practical read ceiling of this device."""
+    buf = torch.zeros(nbytes, dtype=torch.uint8, device=dev)
+    sink = torch.zeros(1, dtype=torch.int32, device=dev)
+    for _ in range(2):
+        pkv.read_probe(buf, sink)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(5):
+        pkv.read_probe(buf, sink)
+    e1.record()
+    torch.cuda.synchronize()
+    gbs = 5 * nbytes / (e0.elapsed_time(e1) * 1e-3) / 1e9
+    del buf
+    torch.cuda.empty_cache()
+    return gbs
+
+
 def copy_probe(torch, dev, nbytes: int = 4 << 30) -> float:
     """Read+write GB/s of a plain device-to-device copy (torch), a practical ceiling."""
     a = torch.empty(nbytes // 2, dtype=torch.uint8, device=dev)
@@ -136,7 +172,7 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
-    ap.add_argument("--workload", default="gqa", choices=["gqa", "opt13b", "long"])
+    ap.add_argument("--workload", default="gqa", choices=["gqa", "opt13b", "long", "cow"])
     ap.add_argument("--partition-size", type=int, default=None)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -173,6 +209,8 @@ def main():
         p, qd, qc, cu = build_long()
         run = run_long(args, p, qd, qc, cu, torch, pkv, workloads, dev)
         return run
+    if args.workload == "cow":
+        return run_cow(args, torch, pkv, workloads, dev)
     W = build_workload(args.workload)
     case = W["decode"]
     part = W["partition_size"] if args.partition_size is None else args.partition_size
@@ -235,6 +273,16 @@ def main():
                      "frac": round(achieved / PEAK_HBM_GBS, 4), "avg_call_ms": round(dec_ms, 4),
                      "traffic": traffic},
     }
+    call_ms = np.array([a.elapsed_time(b) for a, b in evs])
+    res["call_ms_p10_p50_p90"] = [round(float(np.percentile(call_ms, q)), 4) for q in (10, 50, 90)]
+    res["warm_median_GBs"] = round(nbytes / (float(np.median(call_ms)) * 1e-3) / 1e9, 1)
+    cold = cold_calls(torch, pkv, dev, lambda: pkv.paged_attention_decode(out, q, kc, vc, bt, cl, case.scale,
+                                                                        partition_size=part, workspace=ws))
+    res["cold_call_ms_p10_p50_p90"] = [round(float(np.percentile(cold, q)), 4) for q in (10, 50, 90)]
+    res["cold_median_GBs"] = round(nbytes / (float(np.median(cold)) * 1e-3) / 1e9, 1)
+    ceiling = read_ceiling(torch, pkv, dev)
+    res["read_probe_GBs"] = round(ceiling, 1)
+    res["roofline"]["frac_of_read_probe"] = round(achieved / ceiling, 4)
     res["device_copy_GBs"] = round(copy_probe(torch, dev), 1)
     if not args.no_cpu_baseline:
         log("timing the CPU oracle")
@@ -312,6 +360,67 @@ def run_long(args, p, qd, qc, cu, torch, pkv, workloads, dev):
            "roofline": {"bound": "hbm", "kernel": "paged_attention_decode", "achieved":
                         round(nbytes / (dec_ms * 1e-3) / 1e9, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
                         "frac": round(nbytes / (dec_ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4), "traffic": None}}
+    print(json.dumps(res), flush=True)
+
+
+def run_cow(args, torch, pkv, workloads, dev):
+    """Prefix sharing: 16 prompts x 8 samples share their prompt blocks; a step runs
+    the copy-on-write copies, writes every sample's private tokens, then decodes.
+    Logical bytes count each sample's whole context; unique bytes count every
+    distinct (block, kv head) tile once (shared prompt blocks are read by all eight
+    samples, so the logical rate can exceed the HBM peak)."""
+    c = workloads.config_cow()
+    kc = c.pool.key_cache.to(dev)
+    vc = c.pool.value_cache.to(dev)
+    q = c.query.to(dev)
+    bt = torch.from_numpy(c.block_tables).to(dev)
+    cl = torch.from_numpy(c.context_lens).to(dev)
+    bm = torch.from_numpy(c.block_mapping).to(dev)
+    nk, nv = c.new_key.to(dev), c.new_value.to(dev)
+    sm = torch.from_numpy(c.slot_mapping).to(dev)
+    out = torch.empty_like(q)
+    ws = torch.empty(pkv.decode_workspace_size(c.num_seqs, c.num_q_heads, c.num_kv_heads, c.head_dim,
+                                               c.block_size, c.max_blocks_per_seq, 0), dtype=torch.uint8, device=dev)
+    torch.cuda.synchronize()
+
+    def step(ev=None):
+        pkv.copy_blocks([kc], [vc], bm)
+        pkv.reshape_and_cache(nk, nv, kc, vc, sm)
+        if ev is not None:
+            ev[0].record()
+        pkv.paged_attention_decode(out, q, kc, vc, bt, cl, c.scale, workspace=ws)
+        if ev is not None:
+            ev[1].record()
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(evs[i])
+    torch.cuda.synchronize()
+    ms_step = (time.perf_counter() - t0) * 1e3 / args.steps
+    dec_ms = float(np.mean([a.elapsed_time(b) for a, b in evs]))
+    eb = workloads.DTYPES[c.dtype][2]
+    logical = workloads.algorithmic_decode_bytes(c.context_lens, c.num_q_heads, c.num_kv_heads, c.head_dim, eb)
+    nb = (c.context_lens.astype(np.int64) + c.block_size - 1) // c.block_size
+    used = np.unique(np.concatenate([c.block_tables[s, :nb[s]] for s in range(c.num_seqs)]))
+    unique = int(len(used)) * c.num_kv_heads * c.block_size * c.head_dim * 2 * eb
+    res = {"metric": METRIC, "value": round(logical / (ms_step * 1e-3) / 1e9, 1), "unit": "GB/s", "n_gpus": 1,
+           "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_step, 4), "higher_is_better": True,
+           "scaling": "weak", "vs_baseline": None, "dtype": c.dtype, "data": "synthetic",
+           "config": {"workload": "prefix sharing: 16 prompts (1024 - U{1..15} tokens) x 8 samples with U{0..256} "
+                                  "private tokens, GQA 32/8, head_dim 128, bf16; step = copy_blocks of the "
+                                  "copy-on-write pairs + reshape_and_cache of the private tokens + decode",
+                      "num_seqs": c.num_seqs, "cow_pairs": int(c.block_mapping.shape[0])},
+           "decode_ms": round(dec_ms, 4),
+           "logical_bytes": logical, "unique_bytes": unique,
+           "decode_logical_GBs": round(logical / (dec_ms * 1e-3) / 1e9, 1),
+           "decode_unique_GBs": round(unique / (dec_ms * 1e-3) / 1e9, 1),
+           "roofline": {"bound": "hbm", "kernel": "paged_attention_decode (unique tiles)",
+                        "achieved": round(unique / (dec_ms * 1e-3) / 1e9, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                        "frac": round(unique / (dec_ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4), "traffic": None}}
     print(json.dumps(res), flush=True)
 
 

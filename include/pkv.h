@@ -184,6 +184,20 @@ int copy_blocks(void* const* key_caches, void* const* value_caches, int num_laye
                 int num_pairs, int num_kv_heads, int head_dim, int block_size, int num_blocks, int dtype,
                 void* stream);
 
+/*
+ * pkv_read_probe -- measurement utility, not part of the attention path.
+ *
+ * Streams `bytes` bytes of device memory at `buf` with the non-temporal 16-byte
+ * loads the decode kernels use (each wave reads whole 4 KiB tiles, four in
+ * flight), so that a caller can time the practical HBM read ceiling next to a
+ * decode call.
+ *   buf:   device pointer, 16-byte aligned; bytes: a positive multiple of 4096.
+ *   sink:  device buffer of at least 4 bytes; it is written only if the XOR of
+ *          all words read equals 0x9e3779b9 (never for a zero-filled buffer), which
+ *          keeps the loads from being optimised away.
+ */
+int pkv_read_probe(const void* buf, size_t bytes, void* sink, void* stream);
+
 /* Fixed text for a status code. */
 const char* pkv_error_string(int status);
 

@@ -13,6 +13,7 @@ from .pkv import (  # noqa: F401
     load_library,
     paged_attention_chunked,
     paged_attention_decode,
+    read_probe,
     reshape_and_cache,
     version,
 )

@@ -314,4 +314,14 @@ int copy_blocks(void* const* key_caches, void* const* value_caches, int num_laye
     return PKV_OK;
 }
 
+int pkv_read_probe(const void* buf, size_t bytes, void* sink, void* stream) {
+    static const char* fn = "pkv_read_probe";
+    if (!buf || !sink) return fail(PKV_ERR_INVALID, "%s: null pointer argument", fn);
+    if (bytes == 0 || bytes % 4096 != 0) return fail(PKV_ERR_INVALID, "%s: bytes must be a positive multiple of 4096", fn);
+    if (!aligned(buf, 16) || !aligned(sink, 4)) return fail(PKV_ERR_INVALID, "%s: misaligned pointer", fn);
+    hipError_t e = pkv::launch_read_probe(buf, bytes, sink, (hipStream_t)stream);
+    if (e != hipSuccess) return hip_fail(e, fn);
+    return PKV_OK;
+}
+
 }  // extern "C"

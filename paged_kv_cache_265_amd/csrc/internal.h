@@ -69,5 +69,6 @@ hipError_t launch_decode_path(const DecodeParams& p, int kind, int path, hipStre
 hipError_t launch_chunked(const ChunkedParams& p, int kind, hipStream_t stream);
 hipError_t launch_reshape_and_cache(const CacheParams& p, int kind, hipStream_t stream);
 hipError_t launch_copy_blocks(const CopyParams& p, int num_layers, hipStream_t stream);
+hipError_t launch_read_probe(const void* buf, size_t bytes, void* sink, hipStream_t stream);
 
 }  // namespace pkv

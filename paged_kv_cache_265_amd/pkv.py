@@ -32,6 +32,7 @@ SYMBOLS = (
     "paged_attention_chunked",
     "reshape_and_cache",
     "copy_blocks",
+    "pkv_read_probe",
     "pkv_error_string",
     "pkv_last_error",
 )
@@ -69,6 +70,8 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.reshape_and_cache.restype = I
     lib.copy_blocks.argtypes = [P, P, I, P, I, I, I, I, I, I, P]
     lib.copy_blocks.restype = I
+    lib.pkv_read_probe.argtypes = [P, Z, P, P]
+    lib.pkv_read_probe.restype = I
     lib.pkv_error_string.argtypes = [I]
     lib.pkv_error_string.restype = ctypes.c_char_p
     lib.pkv_last_error.argtypes = []
@@ -200,4 +203,13 @@ def copy_blocks(key_caches: Sequence[torch.Tensor], value_caches: Sequence[torch
     vp = (ctypes.c_void_p * max(L, 1))(*[t.data_ptr() for t in value_caches])
     npairs = block_mapping.shape[0] if block_mapping.dim() == 2 else block_mapping.numel() // 2
     rc = load_library().copy_blocks(kp, vp, L, _ptr(block_mapping), npairs, Hkv, D, BS, NB, dt, _stream(stream))
+    _check(rc)
+
+
+def read_probe(buf: torch.Tensor, sink: torch.Tensor, stream=None) -> None:
+    """Stream every byte of `buf` with the decode kernels' load shape (a measurement
+    utility for the practical read ceiling; see include/pkv.h)."""
+    _contig(buf, sink)
+    nbytes = buf.numel() * buf.element_size()
+    rc = load_library().pkv_read_probe(_ptr(buf), nbytes, _ptr(sink), _stream(stream))
     _check(rc)

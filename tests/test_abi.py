@@ -191,6 +191,16 @@ def test_copy_blocks_rejects():
     assert lib.copy_blocks(ok, ok, 2, None, 0, 8, 128, 16, 10, 2, None) == 0  # no pairs: nothing to do
 
 
+def test_read_probe_rejects():
+    lib = pkv.load_library()
+    P = pkv.pkv.ERR_INVALID
+    assert lib.pkv_read_probe(None, 4096, FAKE, None) == P
+    assert lib.pkv_read_probe(FAKE, 4096, None, None) == P
+    assert lib.pkv_read_probe(FAKE, 0, FAKE, None) == P
+    assert lib.pkv_read_probe(FAKE, 4000, FAKE, None) == P      # not a multiple of 4096
+    assert lib.pkv_read_probe(FAKE + 8, 4096, FAKE, None) == P  # misaligned
+
+
 def test_binding_raises_without_library(tmp_path):
     saved = binding._lib
     binding._lib = None

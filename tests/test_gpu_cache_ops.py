@@ -72,3 +72,12 @@ def test_copy_blocks_many_layers_and_empty():
     for layer in range(L):
         assert torch.equal(bits(ks[layer][4]), bits(before[layer][1]))
         assert torch.equal(bits(ks[layer][0]), bits(before[layer][0]))
+
+
+def test_read_probe_runs_and_leaves_sink_alone():
+    """The measurement utility streams a zero buffer without touching its sink."""
+    buf = torch.zeros(3 << 20, dtype=torch.uint8, device="cuda")
+    sink = torch.full((1,), 7, dtype=torch.int32, device="cuda")
+    pkv.read_probe(buf, sink)
+    torch.cuda.synchronize()
+    assert int(sink.item()) == 7
