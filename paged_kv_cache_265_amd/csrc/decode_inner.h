@@ -31,9 +31,12 @@ struct MfmaLoop {
     // ring.  At head_dim 128 one wave per SIMD with a five-tile ring keeps as many
     // bytes in flight as two waves with three tiles each, and its waves progress
     // evenly: two waves on one SIMD share issue slots by age, so with equal work
-    // the younger one finishes far behind the older.
+    // the younger one finishes far behind the older.  Two head tiles (many query
+    // heads per kv head) spend longer on each block, so they keep one more tile in
+    // flight (six tiles x 12 loads stays under the 63 outstanding loads a wave
+    // can count).
     static constexpr int kWaves = (NH == 1 && D == 64) ? 2 : 1;
-    static constexpr int kRing = D == 128 ? 5 : 3;
+    static constexpr int kRing = D == 128 ? (NH == 2 ? 6 : 5) : 3;
 
     struct Tile {
         uint4 k[KS];
