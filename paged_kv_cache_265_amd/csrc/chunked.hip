@@ -9,8 +9,8 @@
 //
 // Rows are (query token, query head of the kv group) pairs, head fastest, so that
 // the heads sharing one kv head share every K/V tile.  A workgroup of 4 waves takes
-// 128 consecutive rows of one (segment, kv head); each wave owns 32 of them (two
-// 16-row matrix-core columns).  The keys go by in steps of 32 (two pool blocks):
+// 256 consecutive rows of one (segment, kv head); each wave owns 64 of them (four
+// 16-row matrix-core columns), so every K/V operand read from LDS serves 64 rows.  The keys go by in steps of 32 (two pool blocks):
 // the workgroup stages a step's K and V into LDS once, double-buffered, and every
 // wave folds it into its rows with an online softmax:
 //   S^T = K Q^T        16x16x32 matrix cores, 16 keys x 16 rows per product
@@ -31,9 +31,9 @@ namespace {
 
 constexpr int NW = 4;                  // waves per workgroup
 constexpr int BS = kBlockSize;
-constexpr int ROWS_PER_WAVE = 32;
+constexpr int NH = 2;                  // 16-row tiles per wave
+constexpr int ROWS_PER_WAVE = 16 * NH;
 constexpr int ROWS_PER_WG = NW * ROWS_PER_WAVE;
-constexpr int NH = ROWS_PER_WAVE / 16;  // 16-row tiles per wave
 constexpr int KSTEP = 2 * BS;          // keys per step
 
 template <int D>
@@ -192,14 +192,15 @@ __global__ __launch_bounds__(NW * 64, 2) void chunked_fa(ChunkedParams p) {
             for (int kh = 0; kh < 2; ++kh)
 #pragma unroll
                 for (int ht = 0; ht < NH; ++ht) sc[kh][ht] = mma_16x16x32<K>(kf[kh][ks], qv[ht][ks], sc[kh][ht]);
-        // V fragments, read while the softmax runs
+        // V fragments, read while the first softmax runs
         uint4 vf[DT];
 #pragma unroll
         for (int dt = 0; dt < DT; ++dt) vf[dt] = *(const uint4*)(vl + (dt * 16 + col) * Lds::VROW + gq * 16);
         // keys of this lane's eight scores: key0 + 4 gq + j and key0 + 16 + 4 gq + j
         const bool masked = key0 + KSTEP - 1 > wave_first_pos;
         const float c = p.scale_log2;
-        uint4 phi[NH], plo[NH];
+        // row tile by row tile: the P.V products of one tile run on the matrix
+        // cores while the next tile's softmax runs on the vector ALU
 #pragma unroll
         for (int ht = 0; ht < NH; ++ht) {
             float s[8];
@@ -239,19 +240,14 @@ __global__ __launch_bounds__(NW * 64, 2) void chunked_fa(ChunkedParams p) {
                                       pr[3] - hi16<K>(h0.y));
             const uint2 l1 = pack4<K>(pr[4] - lo16<K>(h1.x), pr[5] - hi16<K>(h1.x), pr[6] - lo16<K>(h1.y),
                                       pr[7] - hi16<K>(h1.y));
-            phi[ht] = make_uint4(h0.x, h0.y, h1.x, h1.y);
-            plo[ht] = make_uint4(l0.x, l0.y, l1.x, l1.y);
+            const uint4 phi = make_uint4(h0.x, h0.y, h1.x, h1.y);
+            const uint4 plo = make_uint4(l0.x, l0.y, l1.x, l1.y);
+            // high parts, then the remainders: an accumulator is reused DT products later
+#pragma unroll
+            for (int dt = 0; dt < DT; ++dt) acc[ht][dt] = mma_16x16x32<K>(vf[dt], phi, acc[ht][dt]);
+#pragma unroll
+            for (int dt = 0; dt < DT; ++dt) acc[ht][dt] = mma_16x16x32<K>(vf[dt], plo, acc[ht][dt]);
         }
-        // high parts first, then the remainders: an accumulator is reused only
-        // 2 * DT products later
-#pragma unroll
-        for (int dt = 0; dt < DT; ++dt)
-#pragma unroll
-            for (int ht = 0; ht < NH; ++ht) acc[ht][dt] = mma_16x16x32<K>(vf[dt], phi[ht], acc[ht][dt]);
-#pragma unroll
-        for (int dt = 0; dt < DT; ++dt)
-#pragma unroll
-            for (int ht = 0; ht < NH; ++ht) acc[ht][dt] = mma_16x16x32<K>(vf[dt], plo[ht], acc[ht][dt]);
     };
 
     // step s lives in LDS buffer s % 2; its loads were issued two steps earlier

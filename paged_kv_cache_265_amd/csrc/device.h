@@ -168,8 +168,40 @@ __device__ __forceinline__ float read_lane(float v, int src) {
     return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), src));
 }
 
-__device__ __forceinline__ float xor_max(float v, int mask) { return fmaxf(v, __shfl_xor(v, mask, 64)); }
-__device__ __forceinline__ float xor_sum(float v, int mask) { return v + __shfl_xor(v, mask, 64); }
+// v and the value of lane (lane ^ 16) or (lane ^ 32), as a pair: gfx950's row swaps
+// exchange rows 0<->1 and 2<->3 (16-lane rows) or the two 32-lane halves in one
+// vector instruction, without the LDS round trip of a general lane permute.  With
+// both operands equal to v, every lane ends up holding its own value in one result
+// and its partner's in the other.
+__device__ __forceinline__ void swap_pair(float v, int mask, float& a, float& b) {
+    const uint32_t u = __float_as_uint(v);
+    if (mask == 16) {
+        const auto r = __builtin_amdgcn_permlane16_swap(u, u, false, false);
+        a = __uint_as_float(r[0]);
+        b = __uint_as_float(r[1]);
+    } else {
+        const auto r = __builtin_amdgcn_permlane32_swap(u, u, false, false);
+        a = __uint_as_float(r[0]);
+        b = __uint_as_float(r[1]);
+    }
+}
+
+__device__ __forceinline__ float xor_max(float v, int mask) {
+    if (mask == 16 || mask == 32) {
+        float a, b;
+        swap_pair(v, mask, a, b);
+        return fmaxf(a, b);
+    }
+    return fmaxf(v, __shfl_xor(v, mask, 64));
+}
+__device__ __forceinline__ float xor_sum(float v, int mask) {
+    if (mask == 16 || mask == 32) {
+        float a, b;
+        swap_pair(v, mask, a, b);
+        return a + b;
+    }
+    return v + __shfl_xor(v, mask, 64);
+}
 
 constexpr float kLog2e = 1.4426950408889634f;
 // Online softmax with a lazy reference: probabilities are 2^(x - m) with x the
