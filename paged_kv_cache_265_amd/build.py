@@ -17,7 +17,7 @@ LIB = os.path.join(HERE, "libpkv.so")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
 
-SOURCES = ["api.cpp", "decode.hip", "chunked.hip", "cache_ops.hip", "probe.hip"]
+SOURCES = ["api.cpp", "block_manager.cpp", "decode.hip", "chunked.hip", "cache_ops.hip", "probe.hip"]
 
 # packed fp32 instructions are kept out of the generated code on purpose
 COMMON = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}", "-Xclang", "-target-feature", "-Xclang",

@@ -2,6 +2,7 @@
 // argument, then kernel launches on the caller's stream.  No allocation, no
 // synchronisation, no state besides a thread-local error message.
 #include "pkv.h"
+#include "pkv_block_manager.h"
 
 #include <hip/hip_runtime.h>
 
@@ -14,19 +15,25 @@
 #include "internal.h"
 
 namespace {
-
 thread_local char g_msg[512] = "";
+}  // namespace
 
-int fail(int code, const char* fmt, ...) {
+namespace pkv {
+int set_error(int code, const char* fmt, ...) {
     va_list ap;
     va_start(ap, fmt);
     vsnprintf(g_msg, sizeof g_msg, fmt, ap);
     va_end(ap);
     return code;
 }
+}  // namespace pkv
+
+namespace {
+
+using pkv::set_error;
 
 int hip_fail(hipError_t e, const char* what) {
-    return fail(PKV_ERR_HIP, "%s: launch failed: %s", what, hipGetErrorString(e));
+    return set_error(PKV_ERR_HIP, "%s: launch failed: %s", what, hipGetErrorString(e));
 }
 
 bool aligned(const void* p, size_t a) { return ((uintptr_t)p & (a - 1)) == 0; }
@@ -35,20 +42,20 @@ bool dtype_ok(int dt) { return dt == PKV_F32 || dt == PKV_F16 || dt == PKV_BF16;
 
 // Checks shared by every call on the pool geometry.  Returns PKV_OK or a status.
 int check_pool(const char* fn, int num_kv_heads, int head_dim, int block_size, int num_blocks, int dtype) {
-    if (num_kv_heads <= 0) return fail(PKV_ERR_INVALID, "%s: num_kv_heads must be positive (got %d)", fn, num_kv_heads);
-    if (num_blocks <= 0) return fail(PKV_ERR_INVALID, "%s: num_blocks must be positive (got %d)", fn, num_blocks);
-    if (!dtype_ok(dtype)) return fail(PKV_ERR_UNSUPPORTED, "%s: unknown dtype %d", fn, dtype);
+    if (num_kv_heads <= 0) return set_error(PKV_ERR_INVALID, "%s: num_kv_heads must be positive (got %d)", fn, num_kv_heads);
+    if (num_blocks <= 0) return set_error(PKV_ERR_INVALID, "%s: num_blocks must be positive (got %d)", fn, num_blocks);
+    if (!dtype_ok(dtype)) return set_error(PKV_ERR_UNSUPPORTED, "%s: unknown dtype %d", fn, dtype);
     if (head_dim != 64 && head_dim != 128)
-        return fail(PKV_ERR_UNSUPPORTED, "%s: head_dim %d not supported (64 or 128)", fn, head_dim);
+        return set_error(PKV_ERR_UNSUPPORTED, "%s: head_dim %d not supported (64 or 128)", fn, head_dim);
     if (block_size != pkv::kBlockSize)
-        return fail(PKV_ERR_UNSUPPORTED, "%s: block_size %d not supported (16)", fn, block_size);
+        return set_error(PKV_ERR_UNSUPPORTED, "%s: block_size %d not supported (16)", fn, block_size);
     return PKV_OK;
 }
 
 int check_heads(const char* fn, int num_q_heads, int num_kv_heads) {
-    if (num_q_heads <= 0) return fail(PKV_ERR_INVALID, "%s: num_q_heads must be positive (got %d)", fn, num_q_heads);
+    if (num_q_heads <= 0) return set_error(PKV_ERR_INVALID, "%s: num_q_heads must be positive (got %d)", fn, num_q_heads);
     if (num_q_heads % num_kv_heads != 0)
-        return fail(PKV_ERR_INVALID, "%s: num_q_heads %d is not a multiple of num_kv_heads %d", fn, num_q_heads,
+        return set_error(PKV_ERR_INVALID, "%s: num_q_heads %d is not a multiple of num_kv_heads %d", fn, num_q_heads,
                     num_kv_heads);
     return PKV_OK;
 }
@@ -100,6 +107,7 @@ const char* pkv_error_string(int status) {
     case PKV_ERR_UNSUPPORTED: return "unsupported configuration";
     case PKV_ERR_WORKSPACE: return "workspace missing or too small";
     case PKV_ERR_HIP: return "HIP launch failure";
+    case PKV_ERR_NO_BLOCKS: return "no free block in the pool";
     default: return "unknown status";
     }
 }
@@ -144,34 +152,34 @@ int paged_attention_decode(void* out, const void* query, const void* key_cache, 
     int rc;
     if ((rc = check_pool(fn, num_kv_heads, head_dim, block_size, num_blocks, dtype)) != PKV_OK) return rc;
     if ((rc = check_heads(fn, num_q_heads, num_kv_heads)) != PKV_OK) return rc;
-    if (num_seqs < 0) return fail(PKV_ERR_INVALID, "%s: num_seqs must be >= 0 (got %d)", fn, num_seqs);
+    if (num_seqs < 0) return set_error(PKV_ERR_INVALID, "%s: num_seqs must be >= 0 (got %d)", fn, num_seqs);
     if (max_blocks_per_seq <= 0)
-        return fail(PKV_ERR_INVALID, "%s: max_blocks_per_seq must be positive (got %d)", fn, max_blocks_per_seq);
+        return set_error(PKV_ERR_INVALID, "%s: max_blocks_per_seq must be positive (got %d)", fn, max_blocks_per_seq);
     if (!std::isfinite(scale) || !(scale > 0.f))
-        return fail(PKV_ERR_INVALID, "%s: scale must be finite and positive", fn);
+        return set_error(PKV_ERR_INVALID, "%s: scale must be finite and positive", fn);
     if (partition_size < 0 || (partition_size > 0 && partition_size % block_size != 0))
-        return fail(PKV_ERR_INVALID, "%s: partition_size %d must be 0 or a positive multiple of block_size", fn,
+        return set_error(PKV_ERR_INVALID, "%s: partition_size %d must be 0 or a positive multiple of block_size", fn,
                     partition_size);
     const int path = decode_path();
-    if (path < 0) return fail(PKV_ERR_INVALID, "%s: PKV_DECODE_PATH must be auto, valu or mfma", fn);
+    if (path < 0) return set_error(PKV_ERR_INVALID, "%s: PKV_DECODE_PATH must be auto, valu or mfma", fn);
     if (path == 2 && dtype == PKV_F32)
-        return fail(PKV_ERR_UNSUPPORTED, "%s: the matrix-core path takes 16-bit types only", fn);
+        return set_error(PKV_ERR_UNSUPPORTED, "%s: the matrix-core path takes 16-bit types only", fn);
     if (num_seqs == 0) return PKV_OK;
     if (!out || !query || !key_cache || !value_cache || !block_tables || !context_lens)
-        return fail(PKV_ERR_INVALID, "%s: null pointer argument", fn);
+        return set_error(PKV_ERR_INVALID, "%s: null pointer argument", fn);
     if (!aligned(out, 16) || !aligned(query, 16) || !aligned(key_cache, 16) || !aligned(value_cache, 16) ||
         !aligned(block_tables, 4) || !aligned(context_lens, 4))
-        return fail(PKV_ERR_INVALID, "%s: misaligned pointer (16 bytes for tensors, 4 for int32 arrays)", fn);
+        return set_error(PKV_ERR_INVALID, "%s: misaligned pointer (16 bytes for tensors, 4 for int32 arrays)", fn);
     const int mp = partition_size > 0 ? max_parts(max_blocks_per_seq, partition_size) : 0;
     const int G = num_q_heads / num_kv_heads;
     const long long grid = (long long)(mp > 0 ? mp : 1) * num_q_heads * num_seqs;  // bound on workgroups
-    if (grid > 0x7fffffffLL) return fail(PKV_ERR_INVALID, "%s: problem too large for one launch", fn);
+    if (grid > 0x7fffffffLL) return set_error(PKV_ERR_INVALID, "%s: problem too large for one launch", fn);
     const size_t need = pkv_decode_workspace_size(num_seqs, num_q_heads, num_kv_heads, head_dim, block_size,
                                                   max_blocks_per_seq, partition_size);
     if (need > 0 && (!workspace || workspace_bytes < need))
-        return fail(PKV_ERR_WORKSPACE, "%s: workspace of %zu bytes needed, %zu given", fn, need,
+        return set_error(PKV_ERR_WORKSPACE, "%s: workspace of %zu bytes needed, %zu given", fn, need,
                     workspace ? workspace_bytes : (size_t)0);
-    if (need > 0 && !aligned(workspace, 16)) return fail(PKV_ERR_INVALID, "%s: workspace must be 16-byte aligned", fn);
+    if (need > 0 && !aligned(workspace, 16)) return set_error(PKV_ERR_INVALID, "%s: workspace must be 16-byte aligned", fn);
 
     pkv::DecodeParams p;
     p.out = out;
@@ -212,24 +220,24 @@ int paged_attention_chunked(void* out, const void* query, const int32_t* cu_q_le
     int rc;
     if ((rc = check_pool(fn, num_kv_heads, head_dim, block_size, num_blocks, dtype)) != PKV_OK) return rc;
     if ((rc = check_heads(fn, num_q_heads, num_kv_heads)) != PKV_OK) return rc;
-    if (dtype == PKV_F32) return fail(PKV_ERR_UNSUPPORTED, "%s: fp32 is not supported (16-bit types only)", fn);
+    if (dtype == PKV_F32) return set_error(PKV_ERR_UNSUPPORTED, "%s: fp32 is not supported (16-bit types only)", fn);
     if (num_segs < 0 || total_q < 0 || max_q_len < 0)
-        return fail(PKV_ERR_INVALID, "%s: num_segs, total_q and max_q_len must be >= 0", fn);
+        return set_error(PKV_ERR_INVALID, "%s: num_segs, total_q and max_q_len must be >= 0", fn);
     if (max_blocks_per_seq <= 0)
-        return fail(PKV_ERR_INVALID, "%s: max_blocks_per_seq must be positive (got %d)", fn, max_blocks_per_seq);
+        return set_error(PKV_ERR_INVALID, "%s: max_blocks_per_seq must be positive (got %d)", fn, max_blocks_per_seq);
     if (!std::isfinite(scale) || !(scale > 0.f))
-        return fail(PKV_ERR_INVALID, "%s: scale must be finite and positive", fn);
-    if (max_q_len > total_q) return fail(PKV_ERR_INVALID, "%s: max_q_len exceeds total_q", fn);
+        return set_error(PKV_ERR_INVALID, "%s: scale must be finite and positive", fn);
+    if (max_q_len > total_q) return set_error(PKV_ERR_INVALID, "%s: max_q_len exceeds total_q", fn);
     if (num_segs == 0 || total_q == 0 || max_q_len == 0) return PKV_OK;
     if (!out || !query || !cu_q_lens || !key_cache || !value_cache || !block_tables || !context_lens)
-        return fail(PKV_ERR_INVALID, "%s: null pointer argument", fn);
+        return set_error(PKV_ERR_INVALID, "%s: null pointer argument", fn);
     if (!aligned(out, 16) || !aligned(query, 16) || !aligned(key_cache, 16) || !aligned(value_cache, 16) ||
         !aligned(block_tables, 4) || !aligned(context_lens, 4) || !aligned(cu_q_lens, 4))
-        return fail(PKV_ERR_INVALID, "%s: misaligned pointer", fn);
+        return set_error(PKV_ERR_INVALID, "%s: misaligned pointer", fn);
     const int G = num_q_heads / num_kv_heads;
     const long long tiles = ((long long)max_q_len * G + 127) / 128;
     if (tiles * num_kv_heads * num_segs > 0x7fffffffLL)
-        return fail(PKV_ERR_INVALID, "%s: problem too large for one launch", fn);
+        return set_error(PKV_ERR_INVALID, "%s: problem too large for one launch", fn);
     pkv::ChunkedParams p;
     p.out = out;
     p.q = query;
@@ -259,13 +267,13 @@ int reshape_and_cache(const void* key, const void* value, void* key_cache, void*
     static const char* fn = "reshape_and_cache";
     int rc;
     if ((rc = check_pool(fn, num_kv_heads, head_dim, block_size, num_blocks, dtype)) != PKV_OK) return rc;
-    if (num_tokens < 0) return fail(PKV_ERR_INVALID, "%s: num_tokens must be >= 0 (got %d)", fn, num_tokens);
+    if (num_tokens < 0) return set_error(PKV_ERR_INVALID, "%s: num_tokens must be >= 0 (got %d)", fn, num_tokens);
     if (num_tokens == 0) return PKV_OK;
     if (!key || !value || !key_cache || !value_cache || !slot_mapping)
-        return fail(PKV_ERR_INVALID, "%s: null pointer argument", fn);
+        return set_error(PKV_ERR_INVALID, "%s: null pointer argument", fn);
     if (!aligned(key, 16) || !aligned(value, 16) || !aligned(key_cache, 16) || !aligned(value_cache, 16) ||
         !aligned(slot_mapping, 8))
-        return fail(PKV_ERR_INVALID, "%s: misaligned pointer", fn);
+        return set_error(PKV_ERR_INVALID, "%s: misaligned pointer", fn);
     pkv::CacheParams p;
     p.key = key;
     p.value = value;
@@ -287,15 +295,15 @@ int copy_blocks(void* const* key_caches, void* const* value_caches, int num_laye
     int rc;
     if ((rc = check_pool(fn, num_kv_heads, head_dim, block_size, num_blocks, dtype)) != PKV_OK) return rc;
     if (num_layers < 0 || num_pairs < 0)
-        return fail(PKV_ERR_INVALID, "%s: num_layers and num_pairs must be >= 0", fn);
+        return set_error(PKV_ERR_INVALID, "%s: num_layers and num_pairs must be >= 0", fn);
     if (num_layers == 0 || num_pairs == 0) return PKV_OK;
-    if (!key_caches || !value_caches || !block_mapping) return fail(PKV_ERR_INVALID, "%s: null pointer argument", fn);
-    if (!aligned(block_mapping, 8)) return fail(PKV_ERR_INVALID, "%s: misaligned block_mapping", fn);
+    if (!key_caches || !value_caches || !block_mapping) return set_error(PKV_ERR_INVALID, "%s: null pointer argument", fn);
+    if (!aligned(block_mapping, 8)) return set_error(PKV_ERR_INVALID, "%s: misaligned block_mapping", fn);
     for (int l = 0; l < num_layers; ++l) {
         if (!key_caches[l] || !value_caches[l])
-            return fail(PKV_ERR_INVALID, "%s: null cache pointer for layer %d", fn, l);
+            return set_error(PKV_ERR_INVALID, "%s: null cache pointer for layer %d", fn, l);
         if (!aligned(key_caches[l], 16) || !aligned(value_caches[l], 16))
-            return fail(PKV_ERR_INVALID, "%s: misaligned cache pointer for layer %d", fn, l);
+            return set_error(PKV_ERR_INVALID, "%s: misaligned cache pointer for layer %d", fn, l);
     }
     const int esz = dtype == PKV_F32 ? 4 : 2;
     pkv::CopyParams p;
@@ -316,9 +324,9 @@ int copy_blocks(void* const* key_caches, void* const* value_caches, int num_laye
 
 int pkv_read_probe(const void* buf, size_t bytes, void* sink, void* stream) {
     static const char* fn = "pkv_read_probe";
-    if (!buf || !sink) return fail(PKV_ERR_INVALID, "%s: null pointer argument", fn);
-    if (bytes == 0 || bytes % 4096 != 0) return fail(PKV_ERR_INVALID, "%s: bytes must be a positive multiple of 4096", fn);
-    if (!aligned(buf, 16) || !aligned(sink, 4)) return fail(PKV_ERR_INVALID, "%s: misaligned pointer", fn);
+    if (!buf || !sink) return set_error(PKV_ERR_INVALID, "%s: null pointer argument", fn);
+    if (bytes == 0 || bytes % 4096 != 0) return set_error(PKV_ERR_INVALID, "%s: bytes must be a positive multiple of 4096", fn);
+    if (!aligned(buf, 16) || !aligned(sink, 4)) return set_error(PKV_ERR_INVALID, "%s: misaligned pointer", fn);
     hipError_t e = pkv::launch_read_probe(buf, bytes, sink, (hipStream_t)stream);
     if (e != hipSuccess) return hip_fail(e, fn);
     return PKV_OK;

@@ -71,4 +71,7 @@ hipError_t launch_reshape_and_cache(const CacheParams& p, int kind, hipStream_t 
 hipError_t launch_copy_blocks(const CopyParams& p, int num_layers, hipStream_t stream);
 hipError_t launch_read_probe(const void* buf, size_t bytes, void* sink, hipStream_t stream);
 
+// thread-local message of pkv_last_error(); returns code
+int set_error(int code, const char* fmt, ...);
+
 }  // namespace pkv
