@@ -172,7 +172,7 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
-    ap.add_argument("--workload", default="gqa", choices=["gqa", "opt13b", "long", "cow"])
+    ap.add_argument("--workload", default="gqa", choices=["gqa", "opt13b", "long", "cow", "beam"])
     ap.add_argument("--partition-size", type=int, default=None)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -211,6 +211,8 @@ def main():
         return run
     if args.workload == "cow":
         return run_cow(args, torch, pkv, workloads, dev)
+    if args.workload == "beam":
+        return run_beam(args, torch, pkv, workloads, dev)
     W = build_workload(args.workload)
     case = W["decode"]
     part = W["partition_size"] if args.partition_size is None else args.partition_size
@@ -421,6 +423,123 @@ def run_cow(args, torch, pkv, workloads, dev):
            "roofline": {"bound": "hbm", "kernel": "paged_attention_decode (unique tiles)",
                         "achieved": round(unique / (dec_ms * 1e-3) / 1e9, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
                         "frac": round(unique / (dec_ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4), "traffic": None}}
+    print(json.dumps(res), flush=True)
+
+
+def run_beam(args, torch, pkv, workloads, dev):
+    """Beam search over 4 layers: 16 prompts sharing a 256-token system prefix,
+    width 4, one token per beam per step.  The native block manager plans each
+    step (slots, copy-on-write, prefix-cache hits); the GPU runs one copy_blocks
+    for the step's copies, then reshape_and_cache and decode per layer.  Timed:
+    the whole replay of --steps steps (after --warmup steps); the decode calls'
+    logical bytes over their event time give `value`."""
+    from paged_kv_cache_265_amd.block_manager import BlockManager
+    from workloads.beam import make_beam_script
+    total = args.warmup + args.steps
+    sc = make_beam_script(seed=(265, 8), num_prompts=16, system_len=256, tail_len=(128, 512), steps=total,
+                          width=4, num_layers=4, num_q_heads=32, num_kv_heads=8, head_dim=128, decode_every=1)
+    L, Hkv, D, BS = sc.num_layers, sc.num_kv_heads, sc.head_dim, 16
+    NB = 16 * 4 * ((256 + 512 + total) // BS + 2)
+    kcs = [torch.zeros((NB, Hkv, BS, D), dtype=torch.bfloat16, device=dev) for _ in range(L)]
+    vcs = [torch.zeros((NB, Hkv, D, BS), dtype=torch.bfloat16, device=dev) for _ in range(L)]
+    kt, vt = sc.k_table.to(dev), sc.v_table.to(dev)
+    bm = BlockManager(NB, BS)
+    hist = {}
+    pend_slots, pend_pos, pend_ids, pend_copies = [], [], [], []
+    host_s, dec_events, dec_bytes, copies_total, cached_total = 0.0, [], 0, 0, 0
+    ws = None
+
+    def plan(seq, toks):
+        nonlocal host_s
+        t0 = time.perf_counter()
+        slots, copies = bm.append(seq, len(toks))
+        host_s += time.perf_counter() - t0
+        n0 = len(hist[seq])
+        pend_slots.extend(slots)
+        pend_pos.extend(range(n0, n0 + len(toks)))
+        pend_ids.extend(toks)
+        pend_copies.extend(copies)
+        hist[seq].extend(toks)
+
+    step, t_start = 0, None
+    for op in sc.ops:
+        kind = op[0]
+        t0 = time.perf_counter()
+        if kind == "add":
+            prompt = sc.prompts[op[2]]
+            cached = bm.add_sequence(op[1], prompt)
+            host_s += time.perf_counter() - t0
+            cached_total += cached
+            hist[op[1]] = list(prompt[:cached])
+            plan(op[1], list(prompt[cached:]))
+        elif kind == "append":
+            plan(op[1], op[2])
+        elif kind == "fork":
+            bm.fork(op[1], op[2])
+            host_s += time.perf_counter() - t0
+            hist[op[2]] = list(hist[op[1]])
+        elif kind == "free":
+            bm.free_sequence(op[1])
+            host_s += time.perf_counter() - t0
+            del hist[op[1]]
+        elif kind == "commit":
+            bm.commit_prompt(op[1], hist[op[1]])
+            host_s += time.perf_counter() - t0
+        elif kind == "decode":
+            if step == args.warmup:  # the timed region starts after the warm-up steps
+                torch.cuda.synchronize()
+                t_start, host_s, dec_events, dec_bytes, copies_total = time.perf_counter(), 0.0, [], 0, 0
+            if pend_copies:
+                pkv.copy_blocks(kcs, vcs, torch.tensor(pend_copies, dtype=torch.int64, device=dev))
+                copies_total += len(pend_copies)
+            if pend_slots:
+                sm = torch.tensor(pend_slots, dtype=torch.int64, device=dev)
+                pos = torch.tensor(pend_pos, dtype=torch.int64, device=dev)
+                ids = torch.tensor(pend_ids, dtype=torch.int64, device=dev)
+                for l in range(L):
+                    pkv.reshape_and_cache(kt[l, pos, ids].contiguous(), vt[l, pos, ids].contiguous(), kcs[l], vcs[l],
+                                          sm)
+            pend_slots.clear(), pend_pos.clear(), pend_ids.clear(), pend_copies.clear()
+            seqs = sorted(hist)
+            lens = np.array([len(hist[s]) for s in seqs])
+            mb = int(-(-lens.max() // BS))
+            t0 = time.perf_counter()
+            bt_host = np.full((len(seqs), mb), 0x7FFFFFFF, dtype=np.int32)
+            for i, s in enumerate(seqs):
+                row = bm.block_table(s, mb)
+                bt_host[i, :len(row)] = row
+            host_s += time.perf_counter() - t0
+            bt = torch.from_numpy(bt_host).to(dev)
+            cl = torch.from_numpy(lens.astype(np.int32)).to(dev)
+            q = sc.queries[op[1]][:len(seqs)].to(dev).contiguous()
+            need = pkv.decode_workspace_size(len(seqs), 32, 8, 128, BS, mb, 0)
+            if ws is None or ws.numel() < need:
+                ws = torch.empty(need, dtype=torch.uint8, device=dev)
+            out = torch.empty_like(q)
+            for l in range(L):
+                e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                e0.record()
+                pkv.paged_attention_decode(out, q, kcs[l], vcs[l], bt, cl, sc.scale, workspace=ws)
+                e1.record()
+                dec_events.append((e0, e1))
+                dec_bytes += workloads.algorithmic_decode_bytes(lens, 32, 8, 128, 2)
+            step += 1
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t_start
+    dec_ms = sum(a.elapsed_time(b) for a, b in dec_events)
+    nsteps = step - args.warmup
+    res = {"metric": METRIC, "value": round(dec_bytes / (dec_ms * 1e-3) / 1e9, 1), "unit": "GB/s", "n_gpus": 1,
+           "steps": nsteps, "warmup": args.warmup, "ms_per_step": round(wall * 1e3 / nsteps, 4),
+           "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+           "config": {"workload": "beam search, 4 layers: 16 prompts (256-token shared system prefix + U{128..512}), "
+                                  "width 4, GQA 32/8, head_dim 128, bf16; per step the native block manager plans, "
+                                  "then copy_blocks + reshape_and_cache + decode per layer"},
+           "decode_ms_per_step": round(dec_ms / nsteps, 4),
+           "manager_host_us_per_step": round(host_s * 1e6 / nsteps, 1),
+           "cow_copies_timed": copies_total, "prefix_cached_tokens": cached_total,
+           "roofline": {"bound": "hbm", "kernel": "paged_attention_decode", "achieved":
+                        round(dec_bytes / (dec_ms * 1e-3) / 1e9, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                        "frac": round(dec_bytes / (dec_ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4), "traffic": None}}
     print(json.dumps(res), flush=True)
 
 
