@@ -174,6 +174,9 @@ def main():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default="gqa", choices=["gqa", "opt13b", "long", "cow", "beam"])
     ap.add_argument("--partition-size", type=int, default=None)
+    ap.add_argument("--paging-study", action="store_true",
+                    help="time the decode call on the same batch with shuffled and with contiguous block "
+                         "placement, in one process, and print both")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="time a plain 1 GiB device copy (reference kernel for the HBM counters)")
@@ -232,6 +235,8 @@ def main():
         nk, nv, sm = W["new"]
         new = (nk.to(dev), nv.to(dev), torch.from_numpy(sm).to(dev))
     torch.cuda.synchronize()
+    if args.paging_study:
+        return paging_study(args, torch, pkv, workloads, dev, case, kc, vc, q, bt, cl, new, part, ws)
 
     def step(ev=None):
         if new is not None:
@@ -363,6 +368,47 @@ def run_long(args, p, qd, qc, cu, torch, pkv, workloads, dev):
                         round(nbytes / (dec_ms * 1e-3) / 1e9, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
                         "frac": round(nbytes / (dec_ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4), "traffic": None}}
     print(json.dumps(res), flush=True)
+
+
+def paging_study(args, torch, pkv, workloads, dev, case, kc, vc, q, bt, cl, new, part, ws):
+    """The pages report the paged kernel 20-26 % slower than a contiguous one on
+    their GPU ([P1] paging section).  Here: the same batch, the same kernel, with
+    the generator's shuffled block placement and with every sequence's blocks laid
+    out contiguously in logical order (identity placement), timed alternately."""
+    if new is not None:
+        pkv.reshape_and_cache(new[0], new[1], kc, vc, new[2])
+    nb = (case.context_lens.astype(np.int64) + 15) // 16
+    order = np.concatenate([case.block_tables[s, :nb[s]] for s in range(case.num_seqs)]).astype(np.int64)
+    new_id = np.arange(len(order), dtype=np.int32)
+    bt_id = np.full_like(case.block_tables, 0x7FFFFFFF)
+    pos = 0
+    for s in range(case.num_seqs):
+        bt_id[s, :nb[s]] = new_id[pos:pos + nb[s]]
+        pos += nb[s]
+    idx = torch.from_numpy(order).to(dev)
+    kc_id, vc_id = kc[idx].contiguous(), vc[idx].contiguous()
+    bt_id_d = torch.from_numpy(bt_id).to(dev)
+    out = torch.empty_like(q)
+    layouts = {"shuffled": (kc, vc, bt), "contiguous": (kc_id, vc_id, bt_id_d)}
+    times = {k: [] for k in layouts}
+    for rep in range(6):
+        for name, (k_, v_, b_) in layouts.items():
+            for _ in range(3):
+                pkv.paged_attention_decode(out, q, k_, v_, b_, cl, case.scale, partition_size=part, workspace=ws)
+            torch.cuda.synchronize()
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            for _ in range(args.steps):
+                pkv.paged_attention_decode(out, q, k_, v_, b_, cl, case.scale, partition_size=part, workspace=ws)
+            e1.record()
+            torch.cuda.synchronize()
+            times[name].append(e0.elapsed_time(e1) / args.steps)
+    nbytes = workloads.algorithmic_decode_bytes(case.context_lens, case.num_q_heads, case.num_kv_heads,
+                                                case.head_dim, workloads.DTYPES[case.dtype][2])
+    med = {k: float(np.median(v)) for k, v in times.items()}
+    print(json.dumps({"paging_study": args.workload, "call_ms_median": {k: round(v, 4) for k, v in med.items()},
+                      "GBs": {k: round(nbytes / (v * 1e-3) / 1e9, 1) for k, v in med.items()},
+                      "paged_over_contiguous": round(med["shuffled"] / med["contiguous"], 4)}), flush=True)
 
 
 def run_cow(args, torch, pkv, workloads, dev):
