@@ -19,9 +19,13 @@ ARCH = "gfx950"
 
 SOURCES = ["api.cpp", "block_manager.cpp", "decode.hip", "chunked.hip", "cache_ops.hip", "probe.hip"]
 
-# packed fp32 instructions are kept out of the generated code on purpose
+# Packed fp32 instructions are kept out of the generated code on purpose.  Matrix-core
+# accumulators live in ordinary vector registers (VGPR form): the softmax rescales
+# them with vector ALU multiplies, and in the accumulation registers every block
+# would move them back and forth.
 COMMON = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}", "-Xclang", "-target-feature", "-Xclang",
-          "-packed-fp32-ops", "-Wall", "-Werror", "-Wno-unused-command-line-argument", "-I", INCLUDE, "-I", CSRC]
+          "-packed-fp32-ops", "-mllvm", "-amdgpu-mfma-vgpr-form", "-Wall", "-Werror",
+          "-Wno-unused-command-line-argument", "-I", INCLUDE, "-I", CSRC]
 
 
 def _compile(src: str, verbose: bool) -> str:

@@ -559,7 +559,7 @@ hipError_t dispatch(const DecodeParams& p, bool mfma, bool split, hipStream_t st
     if constexpr (K != KF32) {
         if (mfma) {
             if (p.G <= 16) return run<MfmaLoop<K, D, 1>, K>(p, split, base + 0, st);
-            return run<MfmaLoop<K, D, 2>, K>(p, split, base + 1, st);
+            return run<MfmaWideLoop<K, D>, K>(p, split, base + 1, st);
         }
     }
     if (p.G == 1) return run<ValuLoop<K, D, 1>, K>(p, split, base + 2, st);

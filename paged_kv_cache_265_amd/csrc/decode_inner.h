@@ -190,6 +190,201 @@ struct MfmaLoop {
 };
 
 // ---------------------------------------------------------------------------------------
+// Matrix-core inner loop for 17..32 query heads per kv head (MQA-like streams).
+// Scores as in MfmaLoop (two 16-head 16x16x32 products per k-step), but
+//   O^T[d][head] += V^T[d][tokens] . P^T[tokens][head]
+// runs on 32x32x16 products with all 32 heads as columns: the A operand is 8
+// consecutive tokens of one head_dim row -- 16 contiguous bytes of the V tile -- so a
+// tile takes half the V load instructions and a quarter of the P.V products.  The
+// P operand (lane l: head l%32, tokens 8*(l/32)..+7) comes from the score layout
+// (lane l: tokens 4*(l/16)..+3 of head l%16 of each 16-head tile) with one 16-lane
+// row swap per packed word: rows 0/2 keep their head-tile-0 values and take row 1/3's,
+// rows 1/3 take row 0/2's head-tile-1 values and keep their own.
+// ---------------------------------------------------------------------------------------
+template <int K, int D>
+struct MfmaWideLoop {
+    static constexpr int KS = D / 32;
+    static constexpr int DQ = D / 32;  // 32-row head_dim tiles of the output
+    static constexpr int HT = 32;
+    static constexpr int kWaves = 1;
+    // half the V loads of MfmaLoop: at head_dim 128 six tiles fit the register file
+    static constexpr int kRing = D == 128 ? 6 : 8;
+    static constexpr int kTileLoads = KS + DQ;
+
+    struct Tile {
+        uint4 k[KS];
+        uint4 v[DQ];
+    };
+    struct State {
+        float m[2], l[2];
+        f32x16 acc[DQ];
+        uint4 q[2][KS];
+    };
+
+    int lane, col, gq;
+    uint32_t koff, voff;
+
+    __device__ __forceinline__ void init_lane(int ln) {
+        lane = ln;
+        col = ln & 15;
+        gq = ln >> 4;
+        koff = (uint32_t)(col * D + gq * 8) * 2;                 // + ks * 64 bytes
+        voff = (uint32_t)((ln & 31) * kBlockSize + 8 * (ln >> 5)) * 2;  // + dq * 32 rows * 32 bytes
+    }
+
+    __device__ __forceinline__ void start(State& st, const void* q, size_t qrow, int Hq, int head0, int nh) {
+        const uint16_t* qp = (const uint16_t*)q;
+#pragma unroll
+        for (int ht = 0; ht < 2; ++ht) {
+            const int h = ht * 16 + col;
+#pragma unroll
+            for (int ks = 0; ks < KS; ++ks)
+                st.q[ht][ks] = h < nh ? *(const uint4*)(qp + (qrow * Hq + head0 + h) * D + (gq + 4 * ks) * 8)
+                                      : make_uint4(0, 0, 0, 0);
+            st.m[ht] = kNegInf;
+            st.l[ht] = 0.f;
+        }
+#pragma unroll
+        for (int dq = 0; dq < DQ; ++dq)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) st.acc[dq][r] = 0.f;
+    }
+
+    __device__ __forceinline__ void load(Tile& t, const void* kc, const void* vc, size_t tile_index,
+                                         bool live) const {
+        constexpr uint32_t kTile = kBlockSize * D * 2;
+        const size_t base = live ? tile_index * kTile : 0;
+        const rsrc_t kr = tile_rsrc((const char*)kc + base, live ? kTile : 0);
+        const rsrc_t vr = tile_rsrc((const char*)vc + base, live ? kTile : 0);
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) t.k[ks] = stream_load16(kr, koff + ks * 64);
+#pragma unroll
+        for (int dq = 0; dq < DQ; ++dq) t.v[dq] = stream_load16(vr, voff + dq * 32 * kBlockSize * 2);
+    }
+
+    // this lane's output column is head lane % 32: head tile (lane / 16) % 2 (two
+    // scalars, not an array, so that the choice stays a select)
+    __device__ __forceinline__ float pick(float x0, float x1) const { return (lane & 16) ? x1 : x0; }
+
+    __device__ __forceinline__ void block(State& st, Tile& t, int valid, float scale_log2) const {
+        float sv[2][4];
+#pragma unroll
+        for (int ht = 0; ht < 2; ++ht) {
+            f32x4 sc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int ks = 0; ks < KS; ++ks) sc = mma_16x16x32<K>(t.k[ks], st.q[ht][ks], sc);
+#pragma unroll
+            for (int j = 0; j < 4; ++j) sv[ht][j] = sc[j];
+        }
+        if (valid < kBlockSize) {
+#pragma unroll
+            for (int ht = 0; ht < 2; ++ht)
+#pragma unroll
+                for (int j = 0; j < 4; ++j)
+                    if (4 * gq + j >= valid) sv[ht][j] = kNegInf;
+        }
+        float bm[2];
+#pragma unroll
+        for (int ht = 0; ht < 2; ++ht) {
+            bm[ht] = fmaxf(fmaxf(sv[ht][0], sv[ht][1]), fmaxf(sv[ht][2], sv[ht][3]));
+            bm[ht] = xor_max(bm[ht], 16);
+            bm[ht] = xor_max(bm[ht], 32);
+            bm[ht] *= scale_log2;
+        }
+        if (__ballot(bm[0] > st.m[0] + kRescaleSlack || bm[1] > st.m[1] + kRescaleSlack)) {
+            float alpha[2];
+#pragma unroll
+            for (int ht = 0; ht < 2; ++ht) {
+                const float mn = fmaxf(st.m[ht], bm[ht]);
+                alpha[ht] = fast_exp2(st.m[ht] - mn);
+                st.l[ht] *= alpha[ht];
+                st.m[ht] = mn;
+            }
+            const float a = pick(alpha[0], alpha[1]);
+#pragma unroll
+            for (int dq = 0; dq < DQ; ++dq) st.acc[dq] *= a;
+        }
+        uint32_t hi[2][2], lo[2][2];
+#pragma unroll
+        for (int ht = 0; ht < 2; ++ht) {
+            const float off = -st.m[ht];
+            float pr[4];
+#pragma unroll
+            for (int j = 0; j < 4; ++j) pr[j] = fast_exp2(__builtin_fmaf(sv[ht][j], scale_log2, off));
+            st.l[ht] += (pr[0] + pr[1]) + (pr[2] + pr[3]);
+            const uint2 h = pack4<K>(pr[0], pr[1], pr[2], pr[3]);
+            const uint2 r = pack4<K>(pr[0] - lo16<K>(h.x), pr[1] - hi16<K>(h.x), pr[2] - lo16<K>(h.y),
+                                     pr[3] - hi16<K>(h.y));
+            hi[ht][0] = h.x;
+            hi[ht][1] = h.y;
+            lo[ht][0] = r.x;
+            lo[ht][1] = r.y;
+        }
+        // to the P operand layout: tokens 8*(lane/32)..+7 of head lane%32
+        uint4 phi, plo;
+        row_swap16(hi[0][0], hi[1][0], phi.x, phi.z);
+        row_swap16(hi[0][1], hi[1][1], phi.y, phi.w);
+        row_swap16(lo[0][0], lo[1][0], plo.x, plo.z);
+        row_swap16(lo[0][1], lo[1][1], plo.y, plo.w);
+        if (valid < kBlockSize) {
+            const int tk = 8 * (lane >> 5);
+#pragma unroll
+            for (int dq = 0; dq < DQ; ++dq) {
+                uint32_t w[4] = {t.v[dq].x, t.v[dq].y, t.v[dq].z, t.v[dq].w};
+#pragma unroll
+                for (int e = 0; e < 8; ++e)
+                    if (tk + e >= valid) w[e >> 1] &= (e & 1) ? 0x0000ffffu : 0xffff0000u;
+                t.v[dq] = make_uint4(w[0], w[1], w[2], w[3]);
+            }
+        }
+#pragma unroll
+        for (int dq = 0; dq < DQ; ++dq) st.acc[dq] = mma_32x32x16<K>(t.v[dq], phi, st.acc[dq]);
+#pragma unroll
+        for (int dq = 0; dq < DQ; ++dq) st.acc[dq] = mma_32x32x16<K>(t.v[dq], plo, st.acc[dq]);
+    }
+
+    __device__ __forceinline__ void finish(State& st) const {
+#pragma unroll
+        for (int ht = 0; ht < 2; ++ht) st.l[ht] = xor_sum(xor_sum(st.l[ht], 16), 32);
+    }
+
+    // element r of acc[dq] is head_dim row 32*dq + 8*(r/4) + 4*(lane/32) + r%4
+    __device__ __forceinline__ void store_out(const State& st, void* out, size_t orow, int Hq, int head0,
+                                              int nh) const {
+        const int h = lane & 31;
+        if (h >= nh) return;
+        const float lsum = pick(st.l[0], st.l[1]);
+        const float inv = lsum > 0.f ? 1.f / lsum : 0.f;
+        uint16_t* o = (uint16_t*)out + (orow * Hq + head0 + h) * D;
+#pragma unroll
+        for (int dq = 0; dq < DQ; ++dq)
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const f32x16 a = st.acc[dq];
+                *(uint2*)(o + 32 * dq + 8 * j + 4 * (lane >> 5)) =
+                    pack4<K>(a[4 * j] * inv, a[4 * j + 1] * inv, a[4 * j + 2] * inv, a[4 * j + 3] * inv);
+            }
+    }
+
+    __device__ __forceinline__ void store_partial(const State& st, float* rec, int cap, int nh) const {
+        const int h = lane & 31;
+        if (h >= nh) return;
+#pragma unroll
+        for (int dq = 0; dq < DQ; ++dq)
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const f32x16 a = st.acc[dq];
+                *(f32x4*)(rec + h * D + 32 * dq + 8 * j + 4 * (lane >> 5)) =
+                    f32x4{a[4 * j], a[4 * j + 1], a[4 * j + 2], a[4 * j + 3]};
+            }
+        if (lane < 32) {
+            rec[cap * D + h] = pick(st.m[0], st.m[1]);
+            rec[cap * D + cap + h] = pick(st.l[0], st.l[1]);
+        }
+    }
+};
+
+// ---------------------------------------------------------------------------------------
 // Vector-ALU inner loop (fp32, or few query heads per kv head).  Four lanes per
 // token share its dot products (shuffle reductions).  For P.V every load
 // instruction reads 1 KiB of the head_dim-major V tile contiguously: lane l's

@@ -15,6 +15,7 @@ typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
 
 // Element kinds.  Storage is always raw bits; arithmetic is fp32.
 enum Kind { KF32 = 0, KF16 = 1, KBF16 = 2 };
@@ -92,6 +93,28 @@ template <> __device__ __forceinline__ f32x4 mma_16x16x16<KBF16>(uint2 a, uint2 
 template <> __device__ __forceinline__ f32x4 mma_16x16x16<KF16>(uint2 a, uint2 b, f32x4 c) {
     return __builtin_amdgcn_mfma_f32_16x16x16f16(__builtin_bit_cast(f16x4, a), __builtin_bit_cast(f16x4, b), c, 0,
                                                  0, 0);
+}
+
+// 32x32x16 (A: 32 rows x 16 k, 8 elements per lane; lane l holds row l%32,
+// k = 8*(l/32)..+7; B symmetric with columns).  Result: lane l holds column
+// l%32, rows 8*(r/4) + 4*(l/32) + r%4 in element r (r = 0..15).
+template <int K> __device__ __forceinline__ f32x16 mma_32x32x16(uint4 a, uint4 b, f32x16 c);
+template <> __device__ __forceinline__ f32x16 mma_32x32x16<KBF16>(uint4 a, uint4 b, f32x16 c) {
+    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a), __builtin_bit_cast(bf16x8, b), c,
+                                                   0, 0, 0);
+}
+template <> __device__ __forceinline__ f32x16 mma_32x32x16<KF16>(uint4 a, uint4 b, f32x16 c) {
+    return __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8, a), __builtin_bit_cast(f16x8, b), c, 0,
+                                                  0, 0);
+}
+
+// Lanes of rows 0 and 2 (16-lane rows) keep their own value in `a` and receive
+// row 1 / row 3's value of `x` in `b`; lanes of rows 1 and 3 receive row 0 / row
+// 2's value of `y` in `a` and keep their own `y` in `b` (v_permlane16_swap).
+__device__ __forceinline__ void row_swap16(uint32_t x, uint32_t y, uint32_t& a, uint32_t& b) {
+    const auto r = __builtin_amdgcn_permlane16_swap(x, y, false, false);
+    a = r[0];
+    b = r[1];
 }
 
 // ---- streaming loads -----------------------------------------------------------------
