@@ -51,6 +51,9 @@ CASES = [
     ("f16", 16, 1, 128, [640, 19]),
     ("bf16", 32, 1, 128, [2000, 511, 3]),
     ("bf16", 40, 1, 64, [300, 1200]),
+    ("f16", 20, 2, 128, [1, 33, 4000, 250]),    # 32-head P.V loop with the second head tile partly used
+    ("bf16", 17, 1, 64, [16, 47, 2100]),
+    ("f16", 32, 2, 64, [5000, 3, 600]),
 ]
 
 
