@@ -34,7 +34,7 @@ PEAK_HBM_GBS = 8000.0
 PROFILES = os.path.join(ROOT, "profiles")
 # sources of the decode kernels: counter summaries are valid only for these exact files
 KERNEL_SOURCES = [os.path.join(ROOT, "paged_kv_cache_265_amd", "csrc", f)
-                  for f in ("decode.hip", "decode_inner.h", "device.h", "internal.h")]
+                  for f in ("decode.hip", "decode_kernels.h", "decode_inner.h", "device.h", "internal.h")]
 
 
 def log(msg):

@@ -43,7 +43,12 @@
  * caches and output share one type.  Arithmetic is fp32; outputs are rounded to
  * the element type with round-to-nearest-even.
  *
- * Supported: head_dim in {64, 128}, block_size == 16, Hq % Hkv == 0, Hkv >= 1.
+ * Supported: head_dim in {64, 128}, block_size in {8, 16, 32} ([P2] section 1.3
+ * uses 16; the size is the caller's trade of table length against the unused
+ * slots of each sequence's last block), Hq % Hkv == 0, Hkv >= 1.  The attention
+ * kernels work in 16-token tiles at every block size (a tile is one 16-token
+ * block, half of a 32-token block, or two 8-token blocks), so the same logical
+ * K/V gives the same bits at every block size.
  *
  * Conventions for every call:
  *  - Ownership: the caller owns every buffer, the workspace included.  The library
@@ -87,8 +92,8 @@ int pkv_version(void);
 /* Partition length (tokens) that paged_attention_decode uses for the given
  * arguments: partition_size itself when > 0; 0 when partition_size is 0, meaning
  * the balanced split (see paged_attention_decode).  Returns a negative status
- * when block_size <= 0 or partition_size is negative or not a multiple of
- * block_size. */
+ * when block_size <= 0 or partition_size is negative or not a multiple of both
+ * block_size and 16. */
 int pkv_decode_partition_size(int num_seqs, int num_q_heads, int num_kv_heads, int head_dim, int block_size,
                               int max_blocks_per_seq, int partition_size);
 
@@ -120,14 +125,15 @@ size_t pkv_decode_workspace_size(int num_seqs, int num_q_heads, int num_kv_heads
  * sequence ([P3] section 4.2: tiling changes the order of the sums, not the
  * result):
  *   partition_size == 0: balanced split -- the (sequence, kv head, 16-token
- *     block) units of the whole batch are dealt out in equal contiguous ranges to
+ *     tile) units of the whole batch are dealt out in equal contiguous ranges to
  *     as many one-wave workgroups as the GPU holds at once.
  *   partition_size > 0: fixed partitions of that many tokens per sequence.
  *   workspace / workspace_bytes: device buffer of at least
  *   pkv_decode_workspace_size(...) bytes, 16-byte aligned (may be NULL when that
  *   size is 0).  Its contents on entry do not matter and are undefined on
  *   return.  Calls that share a workspace must not overlap in time.
- *   partition_size: 0 or a positive multiple of block_size.
+ *   partition_size: 0 or a positive multiple of both block_size and 16 (a
+ *     partition is whole blocks and whole tiles); otherwise PKV_ERR_INVALID.
  * Results do not depend on partition_size beyond fp32 rounding order, and a
  * given call is deterministic (bit for bit on repeat).
  */

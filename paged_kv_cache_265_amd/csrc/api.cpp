@@ -47,9 +47,15 @@ int check_pool(const char* fn, int num_kv_heads, int head_dim, int block_size, i
     if (!dtype_ok(dtype)) return set_error(PKV_ERR_UNSUPPORTED, "%s: unknown dtype %d", fn, dtype);
     if (head_dim != 64 && head_dim != 128)
         return set_error(PKV_ERR_UNSUPPORTED, "%s: head_dim %d not supported (64 or 128)", fn, head_dim);
-    if (block_size != pkv::kBlockSize)
-        return set_error(PKV_ERR_UNSUPPORTED, "%s: block_size %d not supported (16)", fn, block_size);
+    if (!pkv::supported_block_size(block_size))
+        return set_error(PKV_ERR_UNSUPPORTED, "%s: block_size %d not supported (8, 16 or 32)", fn, block_size);
     return PKV_OK;
+}
+
+// A fixed partition is a whole number of blocks and of 16-token tiles.
+bool partition_ok(int partition_size, int block_size) {
+    const int unit = block_size > pkv::kTileTokens ? block_size : pkv::kTileTokens;
+    return partition_size == 0 || (partition_size > 0 && partition_size % unit == 0);
 }
 
 int check_heads(const char* fn, int num_q_heads, int num_kv_heads) {
@@ -60,8 +66,8 @@ int check_heads(const char* fn, int num_q_heads, int num_kv_heads) {
     return PKV_OK;
 }
 
-int max_parts(int max_blocks_per_seq, int part) {
-    const long long tokens = (long long)max_blocks_per_seq * pkv::kBlockSize;
+int max_parts(int max_blocks_per_seq, int block_size, int part) {
+    const long long tokens = (long long)max_blocks_per_seq * block_size;
     return (int)((tokens + part - 1) / part);
 }
 
@@ -122,15 +128,14 @@ int pkv_decode_partition_size(int num_seqs, int num_q_heads, int num_kv_heads, i
     (void)head_dim;
     (void)max_blocks_per_seq;
     if (block_size <= 0) return PKV_ERR_INVALID;
-    if (partition_size < 0 || (partition_size > 0 && partition_size % block_size != 0)) return PKV_ERR_INVALID;
+    if (!partition_ok(partition_size, block_size)) return PKV_ERR_INVALID;
     return partition_size;  // 0: balanced split sized at launch
 }
 
 size_t pkv_decode_workspace_size(int num_seqs, int num_q_heads, int num_kv_heads, int head_dim, int block_size,
                                  int max_blocks_per_seq, int partition_size) {
     if (num_seqs <= 0 || num_q_heads <= 0 || num_kv_heads <= 0 || num_q_heads % num_kv_heads != 0 ||
-        head_dim <= 0 || block_size <= 0 || max_blocks_per_seq <= 0 || partition_size < 0 ||
-        (partition_size > 0 && partition_size % block_size != 0))
+        head_dim <= 0 || block_size <= 0 || max_blocks_per_seq <= 0 || !partition_ok(partition_size, block_size))
         return 0;
     const int G = num_q_heads / num_kv_heads;
     long long heads_per_kv = 0;
@@ -138,7 +143,7 @@ size_t pkv_decode_workspace_size(int num_seqs, int num_q_heads, int num_kv_heads
     record_shape(G, &heads_per_kv, &cap);
     const size_t per_head = ((size_t)head_dim + 2) * sizeof(float);
     if (partition_size == 0) return split_prefix_bytes(num_seqs) + (size_t)pkv::kMaxSplitWaves * 2 * cap * per_head;
-    const int mp = max_parts(max_blocks_per_seq, partition_size);
+    const int mp = max_parts(max_blocks_per_seq, block_size, partition_size);
     if (mp <= 1) return 0;
     return (size_t)num_seqs * num_kv_heads * heads_per_kv * mp * per_head;
 }
@@ -157,9 +162,9 @@ int paged_attention_decode(void* out, const void* query, const void* key_cache, 
         return set_error(PKV_ERR_INVALID, "%s: max_blocks_per_seq must be positive (got %d)", fn, max_blocks_per_seq);
     if (!std::isfinite(scale) || !(scale > 0.f))
         return set_error(PKV_ERR_INVALID, "%s: scale must be finite and positive", fn);
-    if (partition_size < 0 || (partition_size > 0 && partition_size % block_size != 0))
-        return set_error(PKV_ERR_INVALID, "%s: partition_size %d must be 0 or a positive multiple of block_size", fn,
-                    partition_size);
+    if (!partition_ok(partition_size, block_size))
+        return set_error(PKV_ERR_INVALID, "%s: partition_size %d must be 0 or a positive multiple of block_size and 16",
+                         fn, partition_size);
     const int path = decode_path();
     if (path < 0) return set_error(PKV_ERR_INVALID, "%s: PKV_DECODE_PATH must be auto, valu or mfma", fn);
     if (path == 2 && dtype == PKV_F32)
@@ -170,7 +175,7 @@ int paged_attention_decode(void* out, const void* query, const void* key_cache, 
     if (!aligned(out, 16) || !aligned(query, 16) || !aligned(key_cache, 16) || !aligned(value_cache, 16) ||
         !aligned(block_tables, 4) || !aligned(context_lens, 4))
         return set_error(PKV_ERR_INVALID, "%s: misaligned pointer (16 bytes for tensors, 4 for int32 arrays)", fn);
-    const int mp = partition_size > 0 ? max_parts(max_blocks_per_seq, partition_size) : 0;
+    const int mp = partition_size > 0 ? max_parts(max_blocks_per_seq, block_size, partition_size) : 0;
     const int G = num_q_heads / num_kv_heads;
     const long long grid = (long long)(mp > 0 ? mp : 1) * num_q_heads * num_seqs;  // bound on workgroups
     if (grid > 0x7fffffffLL) return set_error(PKV_ERR_INVALID, "%s: problem too large for one launch", fn);
@@ -202,6 +207,7 @@ int paged_attention_decode(void* out, const void* query, const void* key_cache, 
     p.D = head_dim;
     p.NB = num_blocks;
     p.MB = max_blocks_per_seq;
+    p.BS = block_size;
     p.chunks = 1;
     p.part_tokens = partition_size;
     p.max_parts = mp;
@@ -253,6 +259,7 @@ int paged_attention_chunked(void* out, const void* query, const int32_t* cu_q_le
     p.D = head_dim;
     p.NB = num_blocks;
     p.MB = max_blocks_per_seq;
+    p.BS = block_size;
     p.head_chunk = G;
     p.max_q_len = max_q_len;
     p.scale_log2 = scale * pkv::kLog2eHost;
@@ -283,6 +290,7 @@ int reshape_and_cache(const void* key, const void* value, void* key_cache, void*
     p.num_tokens = num_tokens;
     p.Hkv = num_kv_heads;
     p.D = head_dim;
+    p.BS = block_size;
     hipError_t e = pkv::launch_reshape_and_cache(p, dtype, (hipStream_t)stream);
     if (e != hipSuccess) return hip_fail(e, fn);
     return PKV_OK;

@@ -15,8 +15,6 @@ namespace pkv {
 
 namespace {
 
-constexpr int BS = kBlockSize;
-
 // reshape_and_cache: one workgroup per (group of 16 consecutive tokens, kv head).
 // K rows go straight to their slots (16-byte pieces; a row is contiguous in the
 // token-major tile).  V rows are staged in LDS and written out transposed: 16
@@ -36,6 +34,7 @@ __global__ __launch_bounds__(kCacheThreads) void reshape_and_cache_kernel(CacheP
     const int i0 = g * kTokGroup;
     const int nt = min(kTokGroup, p.num_tokens - i0);
     const int D = p.D;
+    const int BS = p.BS;
     const int row = D * EB + 16;
     const int per_row = D / VE;
 

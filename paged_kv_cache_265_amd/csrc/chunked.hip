@@ -9,9 +9,10 @@
 //
 // Rows are (query token, query head of the kv group) pairs, head fastest, so that
 // the heads sharing one kv head share every K/V tile.  A workgroup of 4 waves takes
-// 256 consecutive rows of one (segment, kv head); each wave owns 64 of them (four
-// 16-row matrix-core columns), so every K/V operand read from LDS serves 64 rows.  The keys go by in steps of 32 (two pool blocks):
-// the workgroup stages a step's K and V into LDS once, double-buffered, and every
+// 128 consecutive rows of one (segment, kv head); each wave owns 32 of them (two
+// 16-row matrix-core columns), so every K/V operand read from LDS serves 32 rows.
+// The keys go by in steps of 32 (two pool blocks of 16 tokens, one of 32, or four of
+// 8): the workgroup stages a step's K and V into LDS once, double-buffered, and every
 // wave folds it into its rows with an online softmax:
 //   S^T = K Q^T        16x16x32 matrix cores, 16 keys x 16 rows per product
 //   O^T += V^T P^T     16x16x32 matrix cores over all 32 keys of the step, P split
@@ -19,9 +20,9 @@
 // LDS layouts (rows padded by 16 bytes, so that the 16 lanes reading one 16-byte
 // column hit 16 distinct bank quads):
 //   K: [32 keys][D] as in the pool tile
-//   V: [D][4 groups][8]: group g holds keys 4g..4g+3 of the first block, then keys
-//      4g..4g+3 of the second -- exactly the 8 keys whose probabilities lane group g
-//      holds after the score product, so one 16-byte read is one matrix-core operand.
+//   V: [D][4 groups][8]: group g holds keys 4g..4g+3 of the step's first 16 keys,
+//      then keys 16+4g..16+4g+3 -- exactly the 8 keys whose probabilities lane group
+//      g holds after the score product, so one 16-byte read is one matrix-core operand.
 #include "device.h"
 #include "internal.h"
 
@@ -30,11 +31,10 @@ namespace pkv {
 namespace {
 
 constexpr int NW = 4;                  // waves per workgroup
-constexpr int BS = kBlockSize;
 constexpr int NH = 2;                  // 16-row tiles per wave
 constexpr int ROWS_PER_WAVE = 16 * NH;
 constexpr int ROWS_PER_WG = NW * ROWS_PER_WAVE;
-constexpr int KSTEP = 2 * BS;          // keys per step
+constexpr int KSTEP = 2 * kTileTokens; // keys per step: two 16-key halves
 
 template <int D>
 struct ChunkLds {
@@ -46,12 +46,16 @@ struct ChunkLds {
     static constexpr int CHUNKS = KSTEP * D * 2 / 16 / (NW * 64);  // 16-byte K (and V) pieces per thread
 };
 
-template <int K, int D>
+// BS: tokens per KV block (8, 16 or 32); a step's 32 keys span KSTEP / BS blocks
+template <int K, int D, int BS>
 __global__ __launch_bounds__(NW * 64, 2) void chunked_fa(ChunkedParams p) {
     constexpr int KS = D / 32;
     constexpr int DT = D / 16;
     using Lds = ChunkLds<D>;
     constexpr uint32_t kTile = BS * D * 2;  // bytes of one (block, kv head) tile
+    constexpr int NBS = KSTEP / BS;         // blocks per step
+    constexpr int kPieces = (int)(kTile / 16);
+    static_assert(kPieces % 64 == 0, "a wave's 64 pieces stay inside one block");
     __shared__ __attribute__((aligned(16))) char lds[2 * Lds::STAGE];
 
     const int G = p.G;
@@ -119,23 +123,32 @@ __global__ __launch_bounds__(NW * 64, 2) void chunked_fa(ChunkedParams p) {
     // loads of blocks past the context are empty (zero bytes, no memory access), so
     // every step issues the same loads and the wait before staging counts exactly
     auto fetch = [&](int step, Staged& r) {
-        const int b0 = step * 2;
-        const bool live0 = b0 < nblk, live1 = b0 + 1 < nblk;
-        const int ph0 = live0 ? scalar_load(table, (size_t)uniform(b0)) : 0;
-        const int ph1 = live1 ? scalar_load(table, (size_t)uniform(b0 + 1)) : 0;
-        const size_t t0 = ((size_t)ph0 * p.Hkv + kvh) * kTile, t1 = ((size_t)ph1 * p.Hkv + kvh) * kTile;
-        const rsrc_t k0 = tile_rsrc((const char*)p.kc + t0, live0 ? kTile : 0);
-        const rsrc_t k1 = tile_rsrc((const char*)p.kc + t1, live1 ? kTile : 0);
-        const rsrc_t v0 = tile_rsrc((const char*)p.vc + t0, live0 ? kTile : 0);
-        const rsrc_t v1 = tile_rsrc((const char*)p.vc + t1, live1 ? kTile : 0);
+        const int b0 = step * NBS;
+        rsrc_t kr[NBS], vr[NBS];
+#pragma unroll
+        for (int b = 0; b < NBS; ++b) {
+            const bool live = b0 + b < nblk;
+            const int ph = live ? scalar_load(table, (size_t)uniform(b0 + b)) : 0;
+            const size_t t = ((size_t)ph * p.Hkv + kvh) * kTile;
+            kr[b] = tile_rsrc((const char*)p.kc + t, live ? kTile : 0);
+            vr[b] = tile_rsrc((const char*)p.vc + t, live ? kTile : 0);
+        }
 #pragma unroll
         for (int i = 0; i < Lds::CHUNKS; ++i) {
-            const int c = tid + i * NW * 64;  // piece c of the step lies in block c / (kTile/16)
-            const uint32_t off = (uint32_t)(c % (kTile / 16)) * 16;
-            // a wave's 64 pieces never straddle the two blocks (kTile/16 is a multiple of 64)
-            const bool second = uniform(c / (int)(kTile / 16)) != 0;
-            r.k[i] = stream_load16(second ? k1 : k0, off);
-            r.v[i] = stream_load16(second ? v1 : v0, off);
+            const int c = tid + i * NW * 64;  // piece c of the step lies in block c / kPieces
+            const uint32_t off = (uint32_t)(c % kPieces) * 16;
+            // a wave's 64 pieces never straddle two blocks: the block is wave-uniform,
+            // and picking its resources is a chain of scalar selects
+            const int blk = uniform(c / kPieces);
+            rsrc_t k = kr[0], v = vr[0];
+#pragma unroll
+            for (int b = 1; b < NBS; ++b)
+                if (blk == b) {
+                    k = kr[b];
+                    v = vr[b];
+                }
+            r.k[i] = stream_load16(k, off);
+            r.v[i] = stream_load16(v, off);
         }
     };
     auto stage = [&](int step, const Staged& r, int buf) {
@@ -144,17 +157,18 @@ __global__ __launch_bounds__(NW * 64, 2) void chunked_fa(ChunkedParams p) {
 #pragma unroll
         for (int i = 0; i < Lds::CHUNKS; ++i) {
             const int c = tid + i * NW * 64;
-            const int blk = c / (int)(kTile / 16);
-            const int off = (c % (int)(kTile / 16)) * 16;
+            const int blk = c / kPieces;
+            const int off = (c % kPieces) * 16;
             // K: key row (within the step), 16-byte column
             const int key = blk * BS + off / (D * 2);
             *(uint4*)(kl + key * Lds::KROW + off % (D * 2)) = r.k[i];
-            // V: head_dim row d, tokens 8h .. 8h+7 of block blk; slots past the
-            // context may hold anything and are zeroed
+            // V: head_dim row d, keys kk .. kk+7 of the step (8 h .. 8 h + 7 of block
+            // blk); slots past the context may hold anything and are zeroed
             const int d = off / (BS * 2);
             const int h = (off % (BS * 2)) / 16;
+            const int kk = blk * BS + 8 * h;
             uint4 v = r.v[i];
-            const int tok0 = step * KSTEP + blk * BS + 8 * h;
+            const int tok0 = step * KSTEP + kk;
             if (tok0 + 8 > n) {
                 uint32_t u[4] = {v.x, v.y, v.z, v.w};
 #pragma unroll
@@ -162,9 +176,12 @@ __global__ __launch_bounds__(NW * 64, 2) void chunked_fa(ChunkedParams p) {
                     if (tok0 + e >= n) u[e / 2] &= (e & 1) ? 0x0000ffffu : 0xffff0000u;
                 v = make_uint4(u[0], u[1], u[2], u[3]);
             }
-            char* vr = vl + d * Lds::VROW + blk * 8;
-            *(uint2*)(vr + (2 * h) * 16) = make_uint2(v.x, v.y);
-            *(uint2*)(vr + (2 * h + 1) * 16) = make_uint2(v.z, v.w);
+            // row d of the LDS V tile: 16-byte chunk j holds keys 4j .. 4j+3 of the
+            // step's first 16-key half, then the same keys of its second half
+            const int jj = (kk % kTileTokens) / 4;
+            char* vrow = vl + d * Lds::VROW + (kk / kTileTokens) * 8;
+            *(uint2*)(vrow + jj * 16) = make_uint2(v.x, v.y);
+            *(uint2*)(vrow + (jj + 1) * 16) = make_uint2(v.z, v.w);
         }
     };
 
@@ -180,7 +197,7 @@ __global__ __launch_bounds__(NW * 64, 2) void chunked_fa(ChunkedParams p) {
         for (int kh = 0; kh < 2; ++kh)
 #pragma unroll
             for (int ks = 0; ks < KS; ++ks)
-                kf[kh][ks] = *(const uint4*)(kl + (kh * BS + col) * Lds::KROW + (gq + 4 * ks) * 16);
+                kf[kh][ks] = *(const uint4*)(kl + (kh * kTileTokens + col) * Lds::KROW + (gq + 4 * ks) * 16);
         f32x4 sc[2][NH];
 #pragma unroll
         for (int kh = 0; kh < 2; ++kh)
@@ -213,7 +230,7 @@ __global__ __launch_bounds__(NW * 64, 2) void chunked_fa(ChunkedParams p) {
 #pragma unroll
                 for (int j = 0; j < 4; ++j) {
                     if (key0 + 4 * gq + j > pos[ht]) s[j] = kNegInf;
-                    if (key0 + BS + 4 * gq + j > pos[ht]) s[4 + j] = kNegInf;
+                    if (key0 + kTileTokens + 4 * gq + j > pos[ht]) s[4 + j] = kNegInf;
                 }
             }
             float bm = fmaxf(fmaxf(fmaxf(s[0], s[1]), fmaxf(s[2], s[3])), fmaxf(fmaxf(s[4], s[5]), fmaxf(s[6], s[7])));
@@ -293,7 +310,12 @@ hipError_t run(const ChunkedParams& p, hipStream_t st) {
     const long long tiles = ((long long)p.max_q_len * p.G + ROWS_PER_WG - 1) / ROWS_PER_WG;
     const long long grid = tiles * p.Hkv * p.num_segs;
     if (grid == 0) return hipSuccess;
-    hipLaunchKernelGGL((chunked_fa<K, D>), dim3((unsigned)grid), dim3(NW * 64), 0, st, p);
+    switch (p.BS) {
+    case 8: hipLaunchKernelGGL((chunked_fa<K, D, 8>), dim3((unsigned)grid), dim3(NW * 64), 0, st, p); break;
+    case 16: hipLaunchKernelGGL((chunked_fa<K, D, 16>), dim3((unsigned)grid), dim3(NW * 64), 0, st, p); break;
+    case 32: hipLaunchKernelGGL((chunked_fa<K, D, 32>), dim3((unsigned)grid), dim3(NW * 64), 0, st, p); break;
+    default: return hipErrorInvalidValue;
+    }
     return hipGetLastError();
 }
 

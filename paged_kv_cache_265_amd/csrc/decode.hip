@@ -1,584 +1,19 @@
-// decode.hip -- paged-attention decode for gfx950.
-//
-// Blockwise attention over a paged KV pool ("每生成一个字都要把全部权重读一遍", section on
-// paging the KV cache, blockwise attention equation): each query head's scores
-// against every cached token of its sequence, one softmax over all of them, and
-// the weighted sum of V, read block by block through the block table.  Online
-// softmax and split contexts reorder the sums without changing what is computed
-// ("LLM 推理优化的系统视角", section 4.2: tiling changes execution order, not
-// semantics).
-//
-// Work is counted in units: one unit is one 16-token block of one stream, a stream
-// being a (sequence, kv head, query-head chunk) triple.  Two schedules:
-//  * balanced split (partition_size == 0): exactly as many one-wave workgroups as
-//    fit on the GPU at once; wave w takes units [w U / N, (w+1) U / N) of the U
-//    units in (sequence, stream, block) order.  It walks them with two blocks in
-//    flight, writes the normalised output of every stream it covers whole, and
-//    leaves (m, l, acc) records for the at most two streams it covers in part (its
-//    first and its last).  A merge kernel joins the pieces of split streams.
-//  * fixed partitions (partition_size > 0): one wave per (stream, partition of
-//    partition_size tokens); multi-partition streams leave one record per
-//    partition for the merge kernel.
-#include "decode_inner.h"
-#include "device.h"
-#include "internal.h"
-
-#include <atomic>
-#include <cstdlib>
+// decode.hip -- paged-attention decode for KV blocks of 16 tokens, and the entry
+// that picks the instantiation for the block size (8 and 32 live in decode_bs8.hip
+// and decode_bs32.hip, compiled separately).
+#include "decode_kernels.h"
 
 namespace pkv {
 
-namespace {
-
-constexpr int BS = kBlockSize;
-
-__device__ __forceinline__ int nblocks(int ctx) { return ctx > 0 ? (ctx + BS - 1) / BS : 0; }
-
-__device__ __forceinline__ int wave_sum_int(int v) {
-#pragma unroll
-    for (int m = 1; m < 64; m <<= 1) v += __shfl_xor(v, m, 64);
-    return v;
+hipError_t launch_decode_bs16(const DecodeParams& p, int kind, int path, hipStream_t st) {
+    return launch_decode_block_size<16>(p, kind, path, st);
 }
-
-__device__ __forceinline__ int wave_incl_scan(int v, int lane) {
-#pragma unroll
-    for (int off = 1; off < 64; off <<= 1) {
-        const int y = __shfl_up(v, off, 64);
-        if (lane >= off) v += y;
-    }
-    return v;
-}
-
-// stream c of a sequence -> first query head and number of heads
-struct Heads {
-    int kvh, head0, nh;
-};
-template <int HT>
-__device__ __forceinline__ Heads stream_heads(const DecodeParams& p, int c) {
-    Heads h;
-    h.kvh = c / p.chunks;
-    const int k = c - h.kvh * p.chunks;
-    h.head0 = h.kvh * p.G + k * HT;
-    h.nh = min(HT, p.G - k * HT);
-    return h;
-}
-
-// sum over all sequences of their block counts
-__device__ long long total_blocks(const DecodeParams& p, int lane) {
-    long long tot = 0;
-    for (int base = 0; base < p.S; base += 64) {
-        const int s = base + lane;
-        tot += wave_sum_int(s < p.S ? nblocks(p.context_lens[s]) : 0);
-    }
-    return tot;
-}
-
-// first wave whose unit range contains unit u (ranges [w U / N, (w+1) U / N))
-__host__ __device__ __forceinline__ long long wave_of(long long u, long long U, long long N) {
-    return ((u + 1) * N - 1) / U;
-}
-
-// ---------------------------------------------------------------------------------------
-// balanced split
-// ---------------------------------------------------------------------------------------
-template <class Loop, int R>
-__global__ __launch_bounds__(64, Loop::kWaves) void decode_split(DecodeParams p) {
-    constexpr int HT = Loop::HT;
-    const int lane = lane_id();
-    const long long N = gridDim.x;
-    const long long w = blockIdx.x;
-    const int NS = p.Hkv * p.chunks;
-    const long long U = total_blocks(p, lane) * NS;
-    const long long lo = w * U / N, hi = (w + 1) * U / N;
-    // starts[s] = unit of sequence s's first block (written by the wave that folds
-    // it), starts[S] = U: the merge finds every stream's pieces from these
-    if (w == 0 && lane == 0) p.starts[p.S] = U;
-    if (lo >= hi) return;
-
-    // locate unit lo: sequence s whose units [NS*cum(s), NS*cum(s+1)) contain it
-    struct Cursor {
-        int s, c, b, nb, ctx;
-    } cur;
-    {
-        long long run = 0;
-        for (int base = 0;; base += 64) {
-            const int s = base + lane;
-            const int ctx = s < p.S ? p.context_lens[s] : 0;
-            const int nb = nblocks(ctx);
-            const int incl = wave_incl_scan(nb, lane);
-            const unsigned long long hit = __ballot(run + (long long)NS * incl > lo);
-            if (hit) {
-                const int t = __builtin_ctzll(hit);
-                cur.s = base + t;
-                cur.nb = read_lane(nb, t);
-                cur.ctx = read_lane(ctx, t);
-                const long long r = lo - (run + (long long)NS * (read_lane(incl, t) - cur.nb));
-                cur.c = (int)(r / cur.nb);
-                cur.b = (int)(r - (long long)cur.c * cur.nb);
-                break;
-            }
-            run += (long long)NS * read_lane(incl, 63);
-        }
-    }
-    auto advance = [&](Cursor& x) {
-        if (++x.b < x.nb) return;
-        x.b = 0;
-        if (++x.c < NS) return;
-        x.c = 0;
-        do {
-            ++x.s;
-            x.ctx = x.s < p.S ? scalar_load(p.context_lens, uniform(x.s)) : BS;
-            x.nb = nblocks(x.ctx);
-        } while (x.nb == 0);
-    };
-
-    Loop L;
-    L.init_lane(lane);
-    typename Loop::State st;
-    const long long cnt = hi - lo;
-    long long issued = 0, done = 0;
-    Cursor ac = cur, cc = cur;
-    const int cap = min(p.G, HT);
-    const size_t rec = (size_t)cap * (p.D + 2);
-    int seg_b0 = cur.b;
-    bool first_seg = true;
-    Heads hd = stream_heads<HT>(p, cur.c);
-
-    // every call issues the loads of one tile -- a real one while units remain,
-    // else an empty one -- so the wait before each fold covers exactly its own tile
-    auto issue = [&](typename Loop::Tile& t) {
-        const bool live = issued < cnt;
-        const int phys = live ? scalar_load(p.block_tables, (size_t)uniform(ac.s) * p.MB + uniform(ac.b)) : 0;
-        L.load(t, p.kc, p.vc, (size_t)phys * p.Hkv + ac.c / p.chunks, live);
-        if (live) {
-            advance(ac);
-            ++issued;
-        }
-    };
-    auto compute = [&](typename Loop::Tile& t) {
-        if (cc.b == 0 && cc.c == 0 && lane == 0) p.starts[cc.s] = lo + done;
-        L.block(st, t, cc.ctx - cc.b * BS, p.scale_log2);
-        if (done + 1 == cnt || cc.b + 1 == cc.nb) {
-            L.finish(st);
-            if (seg_b0 == 0 && cc.b + 1 == cc.nb)
-                L.store_out(st, p.out, cc.s, p.Hq, hd.head0, hd.nh);
-            else
-                L.store_partial(st, p.ws + ((size_t)w * 2 + (first_seg ? 0 : 1)) * rec, cap, hd.nh);
-            first_seg = false;
-        }
-        advance(cc);
-        ++done;
-    };
-    // Issue tile `tn`, then fold tile `tc`.  When tc opens a stream segment its
-    // queries are loaded before tn's tiles, and waited for right there, with tn's
-    // loads left in flight: the state of the previous segment is already stored.
-    auto step = [&](typename Loop::Tile& tn, typename Loop::Tile& tc) {
-        if (done == 0 || cc.b == 0) {
-            seg_b0 = cc.b;
-            hd = stream_heads<HT>(p, cc.c);
-            L.start(st, p.q, cc.s, p.Hq, hd.head0, hd.nh);
-            issue(tn);
-            vm_wait_le<Loop::kTileLoads>();
-        } else {
-            issue(tn);
-        }
-        compute(tc);
-    };
-
-    // ring of R tiles: R - 1 blocks in flight while one is folded
-    typename Loop::Tile ring[R];
-#pragma unroll
-    for (int j = 0; j + 1 < R; ++j) issue(ring[j]);
-    while (done < cnt) {
-#pragma unroll
-        for (int j = 0; j < R; ++j) {
-            step(ring[(j + R - 1) % R], ring[j]);
-            if (done >= cnt) break;
-        }
-    }
-}
-
-// ---------------------------------------------------------------------------------------
-// fixed partitions
-// ---------------------------------------------------------------------------------------
-template <class Loop>
-__global__ __launch_bounds__(64, Loop::kWaves) void decode_fixed(DecodeParams p) {
-    constexpr int HT = Loop::HT;
-    const int NS = p.Hkv * p.chunks;
-    int idx = blockIdx.x;
-    const int part = idx % p.max_parts;
-    idx /= p.max_parts;
-    const int c = idx % NS;
-    const int s = idx / NS;
-    const int ctx = p.context_lens[s];
-    const int nparts = ctx > 0 ? (ctx + p.part_tokens - 1) / p.part_tokens : 1;
-    if (part >= nparts) return;
-    const int t0 = part * p.part_tokens;
-    const int t1 = min(ctx, t0 + p.part_tokens);
-    const int b0 = t0 / BS;
-    const int nb = t1 > t0 ? (t1 - t0 + BS - 1) / BS : 0;
-    const Heads hd = stream_heads<HT>(p, c);
-
-    Loop L;
-    L.init_lane(lane_id());
-    typename Loop::State st;
-    L.start(st, p.q, s, p.Hq, hd.head0, hd.nh);
-    // ring of R tiles, R - 1 blocks in flight while one is folded; past the end
-    // the loads are empty
-    constexpr int R = Loop::kRing;
-    typename Loop::Tile ring[R];
-    auto issue = [&](int i, typename Loop::Tile& t) {
-        const bool live = i < nb;
-        const int phys = live ? scalar_load(p.block_tables, (size_t)s * p.MB + b0 + i) : 0;
-        L.load(t, p.kc, p.vc, (size_t)phys * p.Hkv + hd.kvh, live);
-    };
-#pragma unroll
-    for (int j = 0; j + 1 < R; ++j) issue(j, ring[j]);
-    for (int i = 0; i < nb; i += R) {
-#pragma unroll
-        for (int j = 0; j < R; ++j) {
-            issue(i + j + R - 1, ring[(j + R - 1) % R]);
-            L.block(st, ring[j], t1 - (b0 + i + j) * BS, p.scale_log2);
-            if (i + j + 1 >= nb) break;
-        }
-    }
-    L.finish(st);
-    if (nparts == 1) {
-        L.store_out(st, p.out, s, p.Hq, hd.head0, hd.nh);
-    } else {
-        const int cap = min(p.G, HT);
-        const size_t rec = (size_t)cap * (p.D + 2);
-        L.store_partial(st, p.ws + ((size_t)(s * NS + c) * p.max_parts + part) * rec, cap, hd.nh);
-    }
-}
-
-// ---------------------------------------------------------------------------------------
-// balanced split, streams of few query heads: one workgroup per stream merges
-// all its heads, o = sum_i 2^(m_i - M) acc_i / sum_i 2^(m_i - M) l_i.  Sequences
-// with an empty context get their zero output here.
-// ---------------------------------------------------------------------------------------
-template <int K, int HT>
-__global__ __launch_bounds__(256) void decode_merge_stream(DecodeParams p, int split_waves) {
-    const int NS = p.Hkv * p.chunks;
-    const int stream = blockIdx.x;
-    const int s = stream / NS;
-    const int c = stream - s * NS;
-    const Heads hd = stream_heads<HT>(p, c);
-    const int cap = min(p.G, HT);
-    const int D = p.D;
-    const size_t rec = (size_t)cap * (D + 2);
-    const int ctx = p.context_lens[s];
-
-    // pieces: fixed partitions 0 .. count-1, or the split waves w0 .. w1 (waves
-    // whose unit range is empty wrote nothing; that happens only when U < N)
-    const float* first_rec = nullptr;
-    long long count = 0, w0 = 0, U = 0, a = 0, N = split_waves;
-    if (split_waves == 0) {
-        const int nparts = ctx > 0 ? (ctx + p.part_tokens - 1) / p.part_tokens : 1;
-        if (nparts <= 1) return;
-        first_rec = p.ws + (size_t)(s * NS + c) * p.max_parts * rec;
-        count = nparts;
-    } else {
-        const int nb = nblocks(ctx);
-        if (nb == 0) {  // empty context: zero output
-            for (int e = threadIdx.x; e < hd.nh * D; e += blockDim.x)
-                store_elem<K>(p.out, ((size_t)s * p.Hq + hd.head0) * D + e, 0.f);
-            return;
-        }
-        U = p.starts[p.S];
-        a = p.starts[s] + (long long)c * nb;
-        const long long e = a + nb;
-        w0 = wave_of(a, U, N);
-        const long long w1 = wave_of(e - 1, U, N);
-        if (w0 == w1) return;  // written whole by one wave
-        const long long lo0 = w0 * U / N;
-        first_rec = p.ws + ((size_t)w0 * 2 + (lo0 == a ? 0 : 1)) * rec;  // w0's last segment
-        // U >= N: every wave owns at least one unit, pieces are waves w0 .. w1.
-        // U < N: every non-empty wave owns exactly one unit, pieces are the waves of units a .. e-1.
-        count = U >= N ? w1 - w0 + 1 : nb;
-    }
-    // record of piece i
-    auto record = [&](long long i) -> const float* {
-        if (split_waves == 0) return first_rec + i * rec;
-        if (i == 0) return first_rec;
-        const long long w = U >= N ? w0 + i : wave_of(a + i, U, N);
-        return p.ws + (size_t)w * 2 * rec;  // slot 0: that wave's first segment
-    };
-    // one pass over the pieces, eight at a time so that their loads are in flight
-    // together: (M, L, O) folded online, rescaled by 2^(M_old - M_new)
-    constexpr int CH = 8;
-    for (int e = threadIdx.x; e < hd.nh * D; e += blockDim.x) {
-        const int h = e / D, d = e - h * D;
-        float M = kNegInf, L = 0.f, O = 0.f;
-        for (long long i0 = 0; i0 < count; i0 += CH) {
-            float mv[CH], lv[CH], av[CH];
-#pragma unroll
-            for (int j = 0; j < CH; ++j) {
-                mv[j] = kNegInf;
-                lv[j] = av[j] = 0.f;
-                if (i0 + j < count) {
-                    const float* r = record(i0 + j);
-                    mv[j] = r[cap * D + h];
-                    lv[j] = r[cap * D + cap + h];
-                    av[j] = r[h * D + d];
-                }
-            }
-            float mn = M;
-#pragma unroll
-            for (int j = 0; j < CH; ++j) mn = fmaxf(mn, mv[j]);
-            const float sc = fast_exp2(M - mn);
-            L *= sc;
-            O *= sc;
-#pragma unroll
-            for (int j = 0; j < CH; ++j) {
-                const float wt = fast_exp2(mv[j] - mn);
-                L += wt * lv[j];
-                O += wt * av[j];
-            }
-            M = mn;
-        }
-        store_elem<K>(p.out, ((size_t)s * p.Hq + hd.head0 + h) * D + d, L > 0.f ? O / L : 0.f);
-    }
-}
-
-// ---------------------------------------------------------------------------------------
-// merge of the pieces of a stream, one query head per workgroup:
-//   o = sum_i 2^(m_i - M) acc_i / sum_i 2^(m_i - M) l_i.
-// Pieces: the fixed partitions 0 .. nparts-1 of the stream, or, for the balanced
-// split, the waves w0 .. w1 whose unit ranges cut the stream (w0's last record,
-// then slot 0 of the others; when U < N each unit sits alone in its own wave).
-// 256 threads = 2 groups x 128 head_dim lanes; group g folds pieces g, g+2, ...
-// with the weights 2^(m_i - M) taken from LDS.  Balanced split only: sequences
-// with an empty context get their zero output here.
-// ---------------------------------------------------------------------------------------
-template <int K, int HT>
-__global__ __launch_bounds__(256) void decode_merge_head(DecodeParams p, int split_waves) {
-    constexpr int kRound = 1024;  // pieces folded per round
-    __shared__ const float* ptr[kRound];
-    __shared__ float wts[kRound];
-    __shared__ float red[8];
-    __shared__ float part_o[128];
-    const int NS = p.Hkv * p.chunks;
-    const int cap = min(p.G, HT);
-    int idx = blockIdx.x;
-    const int h = idx % cap;
-    idx /= cap;
-    const int c = idx % NS;
-    const int s = idx / NS;
-    const Heads hd = stream_heads<HT>(p, c);
-    if (h >= hd.nh) return;
-    const int ctx = p.context_lens[s];
-    const int D = p.D;
-    const size_t rec = (size_t)cap * (D + 2);
-    const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
-
-    long long count, w0 = 0, U = 0, a = 0;
-    const long long N = split_waves;
-    const float* first;
-    if (split_waves == 0) {
-        count = ctx > 0 ? (ctx + p.part_tokens - 1) / p.part_tokens : 1;
-        if (count <= 1) return;
-        first = p.ws + (size_t)(s * NS + c) * p.max_parts * rec;
-    } else {
-        const int nb = nblocks(ctx);
-        if (nb == 0) {
-            for (int d = tid; d < D; d += 256) store_elem<K>(p.out, ((size_t)s * p.Hq + hd.head0 + h) * D + d, 0.f);
-            return;
-        }
-        U = p.starts[p.S];
-        a = p.starts[s] + (long long)c * nb;
-        w0 = wave_of(a, U, N);
-        const long long w1 = wave_of(a + nb - 1, U, N);
-        if (w0 == w1) return;  // written whole by one wave
-        first = p.ws + ((size_t)w0 * 2 + (w0 * U / N == a ? 0 : 1)) * rec;  // w0's last segment
-        count = U >= N ? w1 - w0 + 1 : nb;
-    }
-    auto record = [&](long long i) -> const float* {
-        if (split_waves == 0) return first + i * rec;
-        if (i == 0) return first;
-        return p.ws + (size_t)(U >= N ? w0 + i : wave_of(a + i, U, N)) * 2 * rec;
-    };
-    float M = kNegInf;
-    for (long long i = tid; i < count; i += 256) M = fmaxf(M, record(i)[cap * D + h]);
-#pragma unroll
-    for (int m = 1; m < 64; m <<= 1) M = fmaxf(M, __shfl_xor(M, m, 64));
-    if (lane == 0) red[wv] = M;
-    __syncthreads();
-    M = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
-    float L = 0.f, O = 0.f;
-    const int g = tid >> 7, d = tid & 127;
-    for (long long r0 = 0; r0 < count; r0 += kRound) {
-        const int n = (int)min((long long)kRound, count - r0);
-        __syncthreads();
-        for (int i = tid; i < n; i += 256) {
-            const float* r = record(r0 + i);
-            const float w = fast_exp2(r[cap * D + h] - M);
-            ptr[i] = r;
-            wts[i] = w;
-            L += w * r[cap * D + cap + h];
-        }
-        __syncthreads();
-        if (d < D) {
-#pragma unroll 16
-            for (int i = g; i < n; i += 2) O += wts[i] * ptr[i][h * D + d];
-        }
-    }
-#pragma unroll
-    for (int m = 1; m < 64; m <<= 1) L += __shfl_xor(L, m, 64);
-    if (lane == 0) red[4 + wv] = L;
-    if (g == 1) part_o[d] = O;
-    __syncthreads();
-    L = red[4] + red[5] + red[6] + red[7];
-    if (g == 0 && d < D)
-        store_elem<K>(p.out, ((size_t)s * p.Hq + hd.head0 + h) * D + d, L > 0.f ? (O + part_o[d]) / L : 0.f);
-}
-
-// ---------------------------------------------------------------------------------------
-// fixed partitions: merge of one query head of one stream per workgroup (streams
-// can have hundreds of partitions).  256 threads = 2 groups x 128 head_dim lanes;
-// group g folds partitions g, g+2, ...; the weights 2^(m_i - M) come from LDS.
-// ---------------------------------------------------------------------------------------
-template <int K, int HT>
-__global__ __launch_bounds__(256) void decode_merge_fixed(DecodeParams p) {
-    constexpr int kRound = 1024;  // partitions folded per round
-    __shared__ float wts[kRound];
-    __shared__ float red[8];
-    __shared__ float part_o[128];
-    const int NS = p.Hkv * p.chunks;
-    const int cap = min(p.G, HT);
-    int idx = blockIdx.x;
-    const int h = idx % cap;
-    idx /= cap;
-    const int c = idx % NS;
-    const int s = idx / NS;
-    const Heads hd = stream_heads<HT>(p, c);
-    if (h >= hd.nh) return;
-    const int ctx = p.context_lens[s];
-    const int nparts = ctx > 0 ? (ctx + p.part_tokens - 1) / p.part_tokens : 1;
-    if (nparts <= 1) return;
-    const int D = p.D;
-    const size_t rec = (size_t)cap * (D + 2);
-    const float* base = p.ws + (size_t)(s * NS + c) * p.max_parts * rec;
-    const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
-    float M = kNegInf;
-    for (int i = tid; i < nparts; i += 256) M = fmaxf(M, base[i * rec + cap * D + h]);
-#pragma unroll
-    for (int m = 1; m < 64; m <<= 1) M = fmaxf(M, __shfl_xor(M, m, 64));
-    if (lane == 0) red[wv] = M;
-    __syncthreads();
-    M = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
-    float L = 0.f, O = 0.f;
-    const int g = tid >> 7, d = tid & 127;
-    for (int r0 = 0; r0 < nparts; r0 += kRound) {
-        const int n = min(kRound, nparts - r0);
-        __syncthreads();
-        for (int i = tid; i < n; i += 256) {
-            const float* r = base + (size_t)(r0 + i) * rec;
-            const float w = fast_exp2(r[cap * D + h] - M);
-            wts[i] = w;
-            L += w * r[cap * D + cap + h];
-        }
-        __syncthreads();
-        if (d < D) {
-#pragma unroll 16
-            for (int i = g; i < n; i += 2) O += wts[i] * base[(size_t)(r0 + i) * rec + h * D + d];
-        }
-    }
-#pragma unroll
-    for (int m = 1; m < 64; m <<= 1) L += __shfl_xor(L, m, 64);
-    if (lane == 0) red[4 + wv] = L;
-    if (g == 1) part_o[d] = O;
-    __syncthreads();
-    L = red[4] + red[5] + red[6] + red[7];
-    if (g == 0 && d < D)
-        store_elem<K>(p.out, ((size_t)s * p.Hq + hd.head0 + h) * D + d, L > 0.f ? (O + part_o[d]) / L : 0.f);
-}
-
-// ---------------------------------------------------------------------------------------
-// host side
-// ---------------------------------------------------------------------------------------
-
-// one-wave workgroups of kernel f that fit on the current device at once (cached)
-int resident_waves(const void* f, int slot) {
-    static std::atomic<int> cache[64][128];
-    int dev = 0;
-    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) dev = 0;
-    int v = cache[dev][slot].load(std::memory_order_relaxed);
-    if (v > 0) return v;
-    int cus = 0, per_cu = 0;
-    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0) cus = 256;
-    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, f, 64, 0) != hipSuccess || per_cu <= 0) per_cu = 4;
-    v = cus * per_cu;
-    if (v > kMaxSplitWaves) v = kMaxSplitWaves;
-    cache[dev][slot].store(v, std::memory_order_relaxed);
-    return v;
-}
-
-// PKV_SPLIT_DEPTH=2 runs the balanced split with a two-tile ring (one block in
-// flight) instead of the inner loop's own depth; both pipelines stay tested
-bool shallow_split() {
-    const char* e = std::getenv("PKV_SPLIT_DEPTH");
-    return e && e[0] == '2' && e[1] == 0;
-}
-
-template <class Loop, int K>
-hipError_t run(const DecodeParams& p0, bool split, int slot, hipStream_t st) {
-    DecodeParams p = p0;
-    p.chunks = (p.G + Loop::HT - 1) / Loop::HT;
-    const int NS = p.Hkv * p.chunks;
-    int waves = 0;
-    if (split) {
-        if (!shallow_split()) {
-            waves = resident_waves((const void*)decode_split<Loop, Loop::kRing>, slot * 2 + 1);
-            hipLaunchKernelGGL((decode_split<Loop, Loop::kRing>), dim3(waves), dim3(64), 0, st, p);
-        } else {
-            waves = resident_waves((const void*)decode_split<Loop, 2>, slot * 2);
-            hipLaunchKernelGGL((decode_split<Loop, 2>), dim3(waves), dim3(64), 0, st, p);
-        }
-    } else {
-        const long long grid = (long long)p.max_parts * NS * p.S;
-        hipLaunchKernelGGL(decode_fixed<Loop>, dim3((unsigned)grid), dim3(64), 0, st, p);
-    }
-    hipError_t e = hipGetLastError();
-    if (e != hipSuccess || (!split && p.max_parts <= 1)) return e;
-    // few heads per stream: a workgroup per stream; many (MQA-like): one per head
-    const int cap = p.G < Loop::HT ? p.G : Loop::HT;
-    const unsigned per_head = (unsigned)((long long)p.S * NS * cap);
-    if (!split)
-        hipLaunchKernelGGL((decode_merge_fixed<K, Loop::HT>), dim3(per_head), dim3(256), 0, st, p);
-    else if (cap <= 8)
-        hipLaunchKernelGGL((decode_merge_stream<K, Loop::HT>), dim3((unsigned)(p.S * NS)), dim3(256), 0, st, p, waves);
-    else
-        hipLaunchKernelGGL((decode_merge_head<K, Loop::HT>), dim3(per_head), dim3(256), 0, st, p, waves);
-    return hipGetLastError();
-}
-
-template <int K, int D>
-hipError_t dispatch(const DecodeParams& p, bool mfma, bool split, hipStream_t st) {
-    const int base = (K * 2 + (D == 128)) * 5;
-    if constexpr (K != KF32) {
-        if (mfma) {
-            if (p.G <= 16) return run<MfmaLoop<K, D, 1>, K>(p, split, base + 0, st);
-            return run<MfmaWideLoop<K, D>, K>(p, split, base + 1, st);
-        }
-    }
-    if (p.G == 1) return run<ValuLoop<K, D, 1>, K>(p, split, base + 2, st);
-    if (p.G == 2) return run<ValuLoop<K, D, 2>, K>(p, split, base + 3, st);
-    return run<ValuLoop<K, D, 4>, K>(p, split, base + 4, st);
-}
-
-}  // namespace
 
 hipError_t launch_decode_path(const DecodeParams& p, int kind, int path, hipStream_t st) {
-    const bool mfma = kind != KF32 && (path == 2 || (path == 0 && p.G >= 4));
-    const bool split = p.part_tokens == 0;
-    switch (kind * 1000 + p.D) {
-    case KF32 * 1000 + 64: return dispatch<KF32, 64>(p, false, split, st);
-    case KF32 * 1000 + 128: return dispatch<KF32, 128>(p, false, split, st);
-    case KF16 * 1000 + 64: return dispatch<KF16, 64>(p, mfma, split, st);
-    case KF16 * 1000 + 128: return dispatch<KF16, 128>(p, mfma, split, st);
-    case KBF16 * 1000 + 64: return dispatch<KBF16, 64>(p, mfma, split, st);
-    case KBF16 * 1000 + 128: return dispatch<KBF16, 128>(p, mfma, split, st);
+    switch (p.BS) {
+    case 8: return launch_decode_bs8(p, kind, path, st);
+    case 16: return launch_decode_bs16(p, kind, path, st);
+    case 32: return launch_decode_bs32(p, kind, path, st);
     default: return hipErrorInvalidValue;
     }
 }

@@ -13,6 +13,20 @@
 
 namespace pkv {
 
+// Where the 16 tokens of one tile of a (sequence, kv head) are.  Units are
+// (physical block * Hkv + kv head), i.e. (block, kv head) tiles of the pools, each
+// BS * D elements (K: [BS][D] token-major; V: [D][BS] head_dim-major).
+//  * block size 16: the tile is unit u0;
+//  * block size 32: the tile is 16-token half `part` of unit u0;
+//  * block size 8: its tokens 0-7 are unit u0, tokens 8-15 unit u1.
+// An empty source (live = false) loads zeros and reads nothing (block sizes 16, 32),
+// or reads unit 0 of the pools (block size 8); an empty tile is never folded.
+struct TileSrc {
+    size_t u0, u1;
+    int part;
+    bool live;
+};
+
 // ---------------------------------------------------------------------------------------
 // Matrix-core inner loop (16-bit types).  Scores S^T[16 tokens][16 heads] = K Q^T on
 // 16x16x32 MFMA (lane l: token row l%16 of K, head column l%16 of Q, d-chunk
@@ -22,8 +36,9 @@ namespace pkv {
 // A operand is 8 contiguous bytes of the head_dim-major V tile.  P is split into a
 // 16-bit high part and a 16-bit remainder, so the product keeps ~16 bits of P.
 // ---------------------------------------------------------------------------------------
-template <int K, int D, int NH>
+template <int K, int D, int NH, int BS>
 struct MfmaLoop {
+    static constexpr int kBS = BS;
     static constexpr int KS = D / 32;
     static constexpr int DT = D / 16;
     static constexpr int HT = 16 * NH;
@@ -50,13 +65,22 @@ struct MfmaLoop {
     };
 
     int col, gq;
-    uint32_t koff, voff;  // byte offsets of this lane's first K / V piece inside a tile
+    uint32_t koff, voff;  // byte offsets of this lane's first K / V piece inside its unit
+    bool ksel, vsel;      // block size 8: this lane's K row / V tokens lie in unit u1
 
     __device__ __forceinline__ void init_lane(int lane) {
         col = lane & 15;
         gq = lane >> 4;
-        koff = (uint32_t)(col * D + gq * 8) * 2;                // + ks * 64 bytes
-        voff = (uint32_t)(col * kBlockSize + 4 * gq) * 2;        // + dt * 512 bytes
+        if constexpr (BS == 8) {
+            ksel = col >= 8;
+            vsel = gq >= 2;
+            koff = (uint32_t)((col & 7) * D + gq * 8) * 2;  // + ks * 64 bytes
+            voff = (uint32_t)(col * 8 + 4 * (gq & 1)) * 2;   // + dt * 16 rows
+        } else {
+            ksel = vsel = false;
+            koff = (uint32_t)(col * D + gq * 8) * 2;
+            voff = (uint32_t)(col * BS + 4 * gq) * 2;
+        }
     }
 
     // query rows head0 .. head0 + nh - 1 of token row `qrow` (q is [rows][Hq][D])
@@ -76,18 +100,27 @@ struct MfmaLoop {
         }
     }
 
-    // K/V tile `tile_index` of the pools; with live = false the loads return zeros
-    // and read nothing
-    __device__ __forceinline__ void load(Tile& t, const void* kc, const void* vc, size_t tile_index,
-                                         bool live) const {
-        constexpr uint32_t kTile = kBlockSize * D * 2;
-        const size_t base = live ? tile_index * kTile : 0;
-        const rsrc_t kr = tile_rsrc((const char*)kc + base, live ? kTile : 0);
-        const rsrc_t vr = tile_rsrc((const char*)vc + base, live ? kTile : 0);
+    // K/V of the tile `src` names
+    __device__ __forceinline__ void load(Tile& t, const void* kc, const void* vc, const TileSrc& src) const {
+        constexpr size_t kUnit = (size_t)BS * D * 2;
+        if constexpr (BS == 8) {
+            const char* kp = (const char*)kc + (ksel ? src.u1 : src.u0) * kUnit + koff;
+            const char* vp = (const char*)vc + (vsel ? src.u1 : src.u0) * kUnit + voff;
 #pragma unroll
-        for (int ks = 0; ks < KS; ++ks) t.k[ks] = stream_load16(kr, koff + ks * 64);
+            for (int ks = 0; ks < KS; ++ks) t.k[ks] = stream_load16(kp + ks * 64);
 #pragma unroll
-        for (int dt = 0; dt < DT; ++dt) t.v[dt] = stream_load8(vr, voff + dt * 512);
+            for (int dt = 0; dt < DT; ++dt) t.v[dt] = stream_load8(vp + dt * 16 * BS * 2);
+        } else {
+            const size_t kb = src.live ? src.u0 * kUnit + (size_t)src.part * kTileTokens * D * 2 : 0;
+            const size_t vb = src.live ? src.u0 * kUnit + (size_t)src.part * kTileTokens * 2 : 0;
+            const rsrc_t kr = tile_rsrc((const char*)kc + kb, src.live ? kTileTokens * D * 2 : 0);
+            const rsrc_t vr =
+                tile_rsrc((const char*)vc + vb, src.live ? (uint32_t)(kUnit - src.part * kTileTokens * 2) : 0);
+#pragma unroll
+            for (int ks = 0; ks < KS; ++ks) t.k[ks] = stream_load16(kr, koff + ks * 64);
+#pragma unroll
+            for (int dt = 0; dt < DT; ++dt) t.v[dt] = stream_load8(vr, voff + dt * 16 * BS * 2);
+        }
     }
 
     // fold one block whose first `valid` tokens are inside the context
@@ -101,7 +134,7 @@ struct MfmaLoop {
             float sv[4];
 #pragma unroll
             for (int j = 0; j < 4; ++j) sv[j] = sc[j];
-            if (valid < kBlockSize) {
+            if (valid < kTileTokens) {
 #pragma unroll
                 for (int j = 0; j < 4; ++j)
                     if (4 * gq + j >= valid) sv[j] = kNegInf;
@@ -127,7 +160,7 @@ struct MfmaLoop {
             plo[ht] = pack4<K>(pr[0] - lo16<K>(phi[ht].x), pr[1] - hi16<K>(phi[ht].x), pr[2] - lo16<K>(phi[ht].y),
                                pr[3] - hi16<K>(phi[ht].y));
         }
-        if (valid < kBlockSize) {
+        if (valid < kTileTokens) {
             const int tk = 4 * gq;
 #pragma unroll
             for (int dt = 0; dt < DT; ++dt) {
@@ -201,8 +234,9 @@ struct MfmaLoop {
 // row swap per packed word: rows 0/2 keep their head-tile-0 values and take row 1/3's,
 // rows 1/3 take row 0/2's head-tile-1 values and keep their own.
 // ---------------------------------------------------------------------------------------
-template <int K, int D>
+template <int K, int D, int BS>
 struct MfmaWideLoop {
+    static constexpr int kBS = BS;
     static constexpr int KS = D / 32;
     static constexpr int DQ = D / 32;  // 32-row head_dim tiles of the output
     static constexpr int HT = 32;
@@ -223,13 +257,22 @@ struct MfmaWideLoop {
 
     int lane, col, gq;
     uint32_t koff, voff;
+    bool ksel, vsel;  // block size 8: this lane's K row / V tokens lie in unit u1
 
     __device__ __forceinline__ void init_lane(int ln) {
         lane = ln;
         col = ln & 15;
         gq = ln >> 4;
-        koff = (uint32_t)(col * D + gq * 8) * 2;                 // + ks * 64 bytes
-        voff = (uint32_t)((ln & 31) * kBlockSize + 8 * (ln >> 5)) * 2;  // + dq * 32 rows * 32 bytes
+        if constexpr (BS == 8) {
+            ksel = col >= 8;
+            vsel = (ln >> 5) != 0;
+            koff = (uint32_t)((col & 7) * D + gq * 8) * 2;  // + ks * 64 bytes
+            voff = (uint32_t)(ln & 31) * 8 * 2;              // + dq * 32 rows
+        } else {
+            ksel = vsel = false;
+            koff = (uint32_t)(col * D + gq * 8) * 2;
+            voff = (uint32_t)((ln & 31) * BS + 8 * (ln >> 5)) * 2;
+        }
     }
 
     __device__ __forceinline__ void start(State& st, const void* q, size_t qrow, int Hq, int head0, int nh) {
@@ -250,16 +293,26 @@ struct MfmaWideLoop {
             for (int r = 0; r < 16; ++r) st.acc[dq][r] = 0.f;
     }
 
-    __device__ __forceinline__ void load(Tile& t, const void* kc, const void* vc, size_t tile_index,
-                                         bool live) const {
-        constexpr uint32_t kTile = kBlockSize * D * 2;
-        const size_t base = live ? tile_index * kTile : 0;
-        const rsrc_t kr = tile_rsrc((const char*)kc + base, live ? kTile : 0);
-        const rsrc_t vr = tile_rsrc((const char*)vc + base, live ? kTile : 0);
+    __device__ __forceinline__ void load(Tile& t, const void* kc, const void* vc, const TileSrc& src) const {
+        constexpr size_t kUnit = (size_t)BS * D * 2;
+        if constexpr (BS == 8) {
+            const char* kp = (const char*)kc + (ksel ? src.u1 : src.u0) * kUnit + koff;
+            const char* vp = (const char*)vc + (vsel ? src.u1 : src.u0) * kUnit + voff;
 #pragma unroll
-        for (int ks = 0; ks < KS; ++ks) t.k[ks] = stream_load16(kr, koff + ks * 64);
+            for (int ks = 0; ks < KS; ++ks) t.k[ks] = stream_load16(kp + ks * 64);
 #pragma unroll
-        for (int dq = 0; dq < DQ; ++dq) t.v[dq] = stream_load16(vr, voff + dq * 32 * kBlockSize * 2);
+            for (int dq = 0; dq < DQ; ++dq) t.v[dq] = stream_load16(vp + dq * 32 * BS * 2);
+        } else {
+            const size_t kb = src.live ? src.u0 * kUnit + (size_t)src.part * kTileTokens * D * 2 : 0;
+            const size_t vb = src.live ? src.u0 * kUnit + (size_t)src.part * kTileTokens * 2 : 0;
+            const rsrc_t kr = tile_rsrc((const char*)kc + kb, src.live ? kTileTokens * D * 2 : 0);
+            const rsrc_t vr =
+                tile_rsrc((const char*)vc + vb, src.live ? (uint32_t)(kUnit - src.part * kTileTokens * 2) : 0);
+#pragma unroll
+            for (int ks = 0; ks < KS; ++ks) t.k[ks] = stream_load16(kr, koff + ks * 64);
+#pragma unroll
+            for (int dq = 0; dq < DQ; ++dq) t.v[dq] = stream_load16(vr, voff + dq * 32 * BS * 2);
+        }
     }
 
     // this lane's output column is head lane % 32: head tile (lane / 16) % 2 (two
@@ -276,7 +329,7 @@ struct MfmaWideLoop {
 #pragma unroll
             for (int j = 0; j < 4; ++j) sv[ht][j] = sc[j];
         }
-        if (valid < kBlockSize) {
+        if (valid < kTileTokens) {
 #pragma unroll
             for (int ht = 0; ht < 2; ++ht)
 #pragma unroll
@@ -326,7 +379,7 @@ struct MfmaWideLoop {
         row_swap16(hi[0][1], hi[1][1], phi.y, phi.w);
         row_swap16(lo[0][0], lo[1][0], plo.x, plo.z);
         row_swap16(lo[0][1], lo[1][1], plo.y, plo.w);
-        if (valid < kBlockSize) {
+        if (valid < kTileTokens) {
             const int tk = 8 * (lane >> 5);
 #pragma unroll
             for (int dq = 0; dq < DQ; ++dq) {
@@ -408,12 +461,13 @@ template <int K> __device__ __forceinline__ void widen16(uint4 c, float* f) {
     }
 }
 
-template <int K, int D, int GT>
+template <int K, int D, int GT, int BS>
 struct ValuLoop {
+    static constexpr int kBS = BS;
     static constexpr int EB = Elem<K>::bytes;
     static constexpr int VE = 16 / EB;                 // elements per 16-byte chunk
     static constexpr int KC = D / VE / 4;              // K chunks per lane
-    static constexpr int CPR = kBlockSize / VE;        // V chunks per head_dim row (2 or 4)
+    static constexpr int CPR = kTileTokens / VE;       // V chunks per head_dim row of a tile (2 or 4)
     static constexpr int VC = D * CPR / 64;            // V chunks per lane
     static constexpr int HT = GT;
     static constexpr int kWaves = ((D == 128 && (EB == 4 || GT >= 2)) || (EB == 4 && GT == 4)) ? 1 : 2;
@@ -430,12 +484,24 @@ struct ValuLoop {
     };
 
     int lane, tq, sub, tg;
+    uint32_t kt, vt;  // byte offsets of this lane's first K / V chunk inside its unit
+    bool ksel, vsel;  // block size 8: this lane's K row / V tokens lie in unit u1
 
     __device__ __forceinline__ void init_lane(int ln) {
         lane = ln;
         tq = ln >> 2;
         sub = ln & 3;
         tg = ln % CPR;  // which VE tokens of a V row this lane holds
+        if constexpr (BS == 8) {
+            ksel = tq >= 8;
+            vsel = tg >= CPR / 2;
+            kt = (uint32_t)((tq & 7) * D * EB);
+            vt = (uint32_t)((ln / CPR) * 8 * EB + (tg % (CPR / 2)) * 16);
+        } else {
+            ksel = vsel = false;
+            kt = (uint32_t)(tq * D * EB);
+            vt = (uint32_t)((ln / CPR) * BS * EB + tg * 16);
+        }
     }
 
     __device__ __forceinline__ void start(State& st, const void* q, size_t qrow, int Hq, int head0, int nh) {
@@ -455,19 +521,29 @@ struct ValuLoop {
         }
     }
 
-    // K/V tile `tile_index` of the pools; with live = false the loads return zeros
-    // and read nothing
-    __device__ __forceinline__ void load(Tile& t, const void* kc, const void* vc, size_t tile_index,
-                                         bool live) const {
-        constexpr uint32_t kTile = kBlockSize * D * EB;
-        const size_t base = live ? tile_index * kTile : 0;
-        const rsrc_t kr = tile_rsrc((const char*)kc + base, live ? kTile : 0);
-        const rsrc_t vr = tile_rsrc((const char*)vc + base, live ? kTile : 0);
-        const uint32_t kt = (uint32_t)(tq * D * EB), vt = (uint32_t)lane * 16;
+    // K/V of the tile `src` names; V chunk c of this lane is head_dim row
+    // lane / CPR + c * 64 / CPR
+    __device__ __forceinline__ void load(Tile& t, const void* kc, const void* vc, const TileSrc& src) const {
+        constexpr size_t kUnit = (size_t)BS * D * EB;
+        constexpr uint32_t kRowStep = 64 / CPR * BS * EB;  // bytes between V chunks c and c + 1
+        if constexpr (BS == 8) {
+            const char* kp = (const char*)kc + (ksel ? src.u1 : src.u0) * kUnit + kt;
+            const char* vp = (const char*)vc + (vsel ? src.u1 : src.u0) * kUnit + vt;
 #pragma unroll
-        for (int k = 0; k < KC; ++k) t.k[k] = stream_load16(kr, kt + (sub + 4 * k) * 16);
+            for (int k = 0; k < KC; ++k) t.k[k] = stream_load16(kp + (sub + 4 * k) * 16);
 #pragma unroll
-        for (int c = 0; c < VC; ++c) t.v[c] = stream_load16(vr, vt + c * 1024);
+            for (int c = 0; c < VC; ++c) t.v[c] = stream_load16(vp + c * kRowStep);
+        } else {
+            const size_t kb = src.live ? src.u0 * kUnit + (size_t)src.part * kTileTokens * D * EB : 0;
+            const size_t vb = src.live ? src.u0 * kUnit + (size_t)src.part * kTileTokens * EB : 0;
+            const rsrc_t kr = tile_rsrc((const char*)kc + kb, src.live ? kTileTokens * D * EB : 0);
+            const rsrc_t vr =
+                tile_rsrc((const char*)vc + vb, src.live ? (uint32_t)(kUnit - src.part * kTileTokens * EB) : 0);
+#pragma unroll
+            for (int k = 0; k < KC; ++k) t.k[k] = stream_load16(kr, kt + (sub + 4 * k) * 16);
+#pragma unroll
+            for (int c = 0; c < VC; ++c) t.v[c] = stream_load16(vr, vt + c * kRowStep);
+        }
     }
 
     __device__ __forceinline__ void block(State& st, Tile& t, int valid, float scale_log2) const {
@@ -501,7 +577,7 @@ struct ValuLoop {
         float vf[VC][VE];
 #pragma unroll
         for (int c = 0; c < VC; ++c) widen16<K>(t.v[c], vf[c]);
-        if (valid < kBlockSize) {
+        if (valid < kTileTokens) {
 #pragma unroll
             for (int e = 0; e < VE; ++e)
                 if (tg * VE + e >= valid)
@@ -510,9 +586,9 @@ struct ValuLoop {
         }
 #pragma unroll
         for (int j = 0; j < GT; ++j) {
-            float ps[kBlockSize];  // p of every token of the block (wave-uniform)
+            float ps[kTileTokens];  // p of every token of the block (wave-uniform)
 #pragma unroll
-            for (int tk = 0; tk < kBlockSize; ++tk) ps[tk] = read_lane(pj[j], 4 * tk);
+            for (int tk = 0; tk < kTileTokens; ++tk) ps[tk] = read_lane(pj[j], 4 * tk);
 #pragma unroll
             for (int e = 0; e < VE; ++e) {
                 float pe = ps[e];

@@ -164,6 +164,11 @@ __device__ __forceinline__ int lane_id() { return (int)(threadIdx.x & 63); }
 // scalar registers: loads through them are then scalar loads, which the wave waits
 // for separately from its vector loads still in flight.
 __device__ __forceinline__ int uniform(int v) { return __builtin_amdgcn_readfirstlane(v); }
+__device__ __forceinline__ long long uniform(long long v) {
+    const uint64_t lo = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)v);
+    const uint64_t hi = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)((uint64_t)v >> 32));
+    return (long long)(lo | (hi << 32));
+}
 
 // Wait until every vector memory access of this wave has completed (s_waitcnt
 // vmcnt(0); the expcnt and lgkmcnt fields are left at their maximum).  Placed

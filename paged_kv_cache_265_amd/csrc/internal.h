@@ -8,7 +8,11 @@
 
 namespace pkv {
 
-constexpr int kBlockSize = 16;  // tokens per KV block (the only block size compiled)
+// The attention kernels work in tiles of 16 tokens of one kv head.  A KV block of
+// 16 tokens is one tile, a block of 32 tokens holds two, and a tile spans two blocks
+// of 8 tokens.
+constexpr int kTileTokens = 16;
+inline bool supported_block_size(int bs) { return bs == 8 || bs == 16 || bs == 32; }
 constexpr float kLog2eHost = 1.4426950408889634f;
 
 struct DecodeParams {
@@ -21,9 +25,10 @@ struct DecodeParams {
     float* ws;        // partial records: acc[cap][D], m[cap], l[cap] (m in log2 units)
     long long* starts;  // balanced split: first unit of every sequence, then the unit count
     int S, Hq, Hkv, G, D, NB, MB;
+    int BS;           // tokens per KV block: 8, 16 or 32
     int chunks;       // query-head chunks per kv head (set by the launcher)
-    int part_tokens;  // 0: balanced split; else tokens per fixed partition (multiple of kBlockSize)
-    int max_parts;    // fixed partitions: ceil(MB * kBlockSize / part_tokens)
+    int part_tokens;  // 0: balanced split; else tokens per fixed partition (multiple of 16 and of BS)
+    int max_parts;    // fixed partitions: ceil(MB * BS / part_tokens)
     float scale_log2; // scale * log2(e): scores are kept in log2 units
 };
 
@@ -39,6 +44,7 @@ struct ChunkedParams {
     const int32_t* block_tables;
     const int32_t* context_lens;
     int num_segs, Hq, Hkv, G, D, NB, MB;
+    int BS;           // tokens per KV block: 8, 16 or 32
     int head_chunk;   // query heads of one group handled together (<= G)
     int max_q_len;
     float scale_log2;
@@ -50,7 +56,7 @@ struct CacheParams {
     void* kc;
     void* vc;
     const int64_t* slots;
-    int num_tokens, Hkv, D;
+    int num_tokens, Hkv, D, BS;
 };
 
 constexpr int kMaxLayersPerLaunch = 32;
@@ -66,6 +72,10 @@ struct CopyParams {
 hipError_t launch_decode(const DecodeParams& p, int kind, hipStream_t stream);
 // path: 0 automatic, 1 vector ALU inner loop, 2 matrix-core inner loop (16-bit types)
 hipError_t launch_decode_path(const DecodeParams& p, int kind, int path, hipStream_t stream);
+// the same for one block size (one translation unit each)
+hipError_t launch_decode_bs8(const DecodeParams& p, int kind, int path, hipStream_t stream);
+hipError_t launch_decode_bs16(const DecodeParams& p, int kind, int path, hipStream_t stream);
+hipError_t launch_decode_bs32(const DecodeParams& p, int kind, int path, hipStream_t stream);
 hipError_t launch_chunked(const ChunkedParams& p, int kind, hipStream_t stream);
 hipError_t launch_reshape_and_cache(const CacheParams& p, int kind, hipStream_t stream);
 hipError_t launch_copy_blocks(const CopyParams& p, int num_layers, hipStream_t stream);

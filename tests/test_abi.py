@@ -67,6 +67,15 @@ def test_workspace_size_matches_layout():
     assert pkv.decode_partition_size(1, 1, 1, 64, 16, 8, 48) == 48
     with pytest.raises(pkv.PkvError):
         pkv.decode_partition_size(1, 1, 1, 64, 16, 8, 40)  # not a multiple of the block size
+    # other block sizes: max_blocks_per_seq counts blocks of that size
+    assert pkv.decode_workspace_size(8, 8, 8, 64, 32, 16, partition_size=512) == 0
+    assert pkv.decode_workspace_size(8, 8, 8, 64, 32, 17, partition_size=512) == 8 * 8 * 2 * rec(1, 64)
+    assert pkv.decode_workspace_size(8, 8, 8, 64, 8, 65, partition_size=512) == 8 * 8 * 2 * rec(1, 64)
+    assert pkv.decode_partition_size(1, 1, 1, 64, 8, 8, 32) == 32
+    with pytest.raises(pkv.PkvError):
+        pkv.decode_partition_size(1, 1, 1, 64, 8, 8, 24)  # a whole number of blocks, not of 16-token tiles
+    with pytest.raises(pkv.PkvError):
+        pkv.decode_partition_size(1, 1, 1, 64, 32, 8, 48)
 
 
 def _decode(**over):
@@ -103,8 +112,14 @@ DECODE_BAD = [
     ({"block_tables": FAKE + 2}, pkv.pkv.ERR_INVALID),
     ({"head_dim": 96}, pkv.pkv.ERR_UNSUPPORTED),
     ({"head_dim": 256}, pkv.pkv.ERR_UNSUPPORTED),
-    ({"block_size": 32}, pkv.pkv.ERR_UNSUPPORTED),
+    ({"block_size": 24}, pkv.pkv.ERR_UNSUPPORTED),
+    ({"block_size": 64}, pkv.pkv.ERR_UNSUPPORTED),
+    ({"block_size": 0}, pkv.pkv.ERR_UNSUPPORTED),
     ({"dtype": 7}, pkv.pkv.ERR_UNSUPPORTED),
+    # a fixed partition is a whole number of blocks and of 16-token tiles
+    ({"partition_size": 24}, pkv.pkv.ERR_INVALID),
+    ({"block_size": 8, "partition_size": 8}, pkv.pkv.ERR_INVALID),
+    ({"block_size": 32, "partition_size": 16}, pkv.pkv.ERR_INVALID),
     # 4 blocks x 16 tokens fit one 512-token partition: no workspace; force 2 partitions
     ({"partition_size": 32}, pkv.pkv.ERR_WORKSPACE),
     ({"partition_size": 32, "workspace": FAKE, "workspace_bytes": 100}, pkv.pkv.ERR_WORKSPACE),
@@ -144,6 +159,7 @@ def _chunked(**over):
     ({"cu_q_lens": None}, pkv.pkv.ERR_INVALID),
     ({"num_q_heads": 7, "num_kv_heads": 2}, pkv.pkv.ERR_INVALID),
     ({"head_dim": 80}, pkv.pkv.ERR_UNSUPPORTED),
+    ({"block_size": 4}, pkv.pkv.ERR_UNSUPPORTED),
     ({"scale": 0.0}, pkv.pkv.ERR_INVALID),
     ({"out": FAKE + 4}, pkv.pkv.ERR_INVALID),
 ])
@@ -169,7 +185,7 @@ def _rac(**over):
     ({"slot_mapping": FAKE + 4}, pkv.pkv.ERR_INVALID),
     ({"value": FAKE + 8}, pkv.pkv.ERR_INVALID),
     ({"num_kv_heads": 0}, pkv.pkv.ERR_INVALID),
-    ({"block_size": 8}, pkv.pkv.ERR_UNSUPPORTED),
+    ({"block_size": 12}, pkv.pkv.ERR_UNSUPPORTED),
     ({"dtype": 3}, pkv.pkv.ERR_UNSUPPORTED),
 ])
 def test_reshape_and_cache_rejects(over, code):
@@ -188,6 +204,7 @@ def test_copy_blocks_rejects():
     assert lib.copy_blocks(ok, ok, 2, FAKE + 4, 1, 8, 128, 16, 10, 2, None) == pkv.pkv.ERR_INVALID
     assert lib.copy_blocks(ok, ok, -1, FAKE, 1, 8, 128, 16, 10, 2, None) == pkv.pkv.ERR_INVALID
     assert lib.copy_blocks(ok, ok, 2, FAKE, 1, 8, 100, 16, 10, 2, None) == pkv.pkv.ERR_UNSUPPORTED
+    assert lib.copy_blocks(ok, ok, 2, FAKE, 1, 8, 128, 48, 10, 2, None) == pkv.pkv.ERR_UNSUPPORTED
     assert lib.copy_blocks(ok, ok, 2, None, 0, 8, 128, 16, 10, 2, None) == 0  # no pairs: nothing to do
 
 

@@ -1,0 +1,186 @@
+"""GPU parity at KV block sizes 8 and 32 (16 is covered everywhere else).
+
+The kernels work on 16-token tiles whatever the block size: a 32-token block holds
+two tiles, and a tile spans two 8-token blocks.  Tiles are folded in the same order
+at every block size, so besides agreeing with the oracle, the outputs for the same
+logical K/V must be identical bit for bit across block sizes.  Every case prints
+what it runs before it launches anything."""
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import paged_kv_cache_265_amd as pkv
+from workloads.gen import DTYPES, make_chunked_case, make_decode_case, new_pool, reblock
+
+from helpers import bits, check_close, dev
+
+pytestmark = pytest.mark.gpu
+
+
+def say(msg):
+    print(msg, flush=True)
+
+
+def decode_on(paged, case, partition_size=0):
+    bs = paged.pool.block_size
+    say(f"decode bs={bs} {case.dtype} S={case.num_seqs} Hq={case.num_q_heads} Hkv={case.num_kv_heads} "
+        f"D={case.head_dim} part={partition_size} ctx={paged.context_lens.tolist()}")
+    q = dev(case.query)
+    out = torch.full_like(q, float("nan"))
+    pkv.paged_attention_decode(out, q, dev(paged.pool.key_cache), dev(paged.pool.value_cache),
+                               dev(paged.block_tables), dev(paged.context_lens), case.scale,
+                               partition_size=partition_size)
+    torch.cuda.synchronize()
+    return out
+
+
+def oracle_on(paged, case):
+    return oracle.decode(case.query, paged.pool.key_cache, paged.pool.value_cache, paged.block_tables,
+                         paged.context_lens, case.num_kv_heads, paged.pool.block_size, case.scale, case.dtype)
+
+
+# (dtype, G, Hkv, D, context lengths): every inner loop (vector ALU for 1-2 heads per
+# kv head and fp32, 16-head and 32-head matrix-core loops), both head dims, contexts
+# ending on and off 8-, 16- and 32-token edges (an odd count of 8-token blocks leaves
+# a tile whose second block does not exist)
+CASES = [
+    ("f32", 1, 4, 64, [1, 7, 8, 9, 33]),
+    ("f16", 1, 2, 128, [24, 200, 513]),
+    ("bf16", 2, 2, 128, [40, 1000, 17]),
+    ("bf16", 4, 8, 128, [1, 8, 15, 16, 17, 24, 32, 512, 520, 1500]),
+    ("f16", 4, 2, 64, [77, 1032, 9]),
+    ("bf16", 16, 1, 128, [640, 23]),
+    ("bf16", 32, 1, 128, [2000, 511, 3, 40]),
+    ("f16", 20, 2, 64, [1, 33, 1100, 250]),
+]
+
+
+@pytest.mark.parametrize("bs", [8, 32])
+@pytest.mark.parametrize("dtype,G,Hkv,D,ctx", CASES)
+def test_decode_block_size_matches_oracle_and_bs16(bs, dtype, G, Hkv, D, ctx):
+    case = make_decode_case([61, G, D, len(ctx)], dtype, ctx, G * Hkv, Hkv, D)
+    p = reblock(case.paged, bs, np.random.default_rng([62, bs, G]))
+    ref = oracle_on(p, case)
+    np.testing.assert_array_equal(ref, oracle_on(case.paged, case))  # the oracle does not see block sizes
+    for part in (0, 64):
+        out = decode_on(p, case, part)
+        check_close(out, ref, dtype, f"bs={bs} part={part}")
+        # same tiles in the same order as at block size 16: the same bits
+        assert torch.equal(bits(out), bits(decode_on(case.paged, case, part))), f"bs={bs} part={part} vs 16"
+
+
+@pytest.mark.parametrize("bs", [8, 32])
+@pytest.mark.parametrize("path", ["valu", "mfma"])
+def test_decode_block_size_both_inner_loops(bs, path, monkeypatch):
+    monkeypatch.setenv("PKV_DECODE_PATH", path)
+    case = make_decode_case([63, bs], "bf16", [5, 300, 1025, 64], 8, 2, 128)
+    p = reblock(case.paged, bs, np.random.default_rng(bs))
+    check_close(decode_on(p, case), oracle_on(p, case), "bf16", f"{path} bs={bs}")
+
+
+@pytest.mark.parametrize("bs", [8, 32])
+def test_decode_block_size_partition_sweep(bs):
+    """Fixed partitions of 32 to 2048 tokens (whole blocks and tiles) and the balanced split."""
+    case = make_decode_case([64, bs], "bf16", [1, 40, 333, 1200, 2048], 8, 2, 128)
+    p = reblock(case.paged, bs, np.random.default_rng(bs))
+    ref = oracle_on(p, case)
+    for part in (32, 64, 96, 160, 512, 2048, 0):
+        check_close(decode_on(p, case, part), ref, "bf16", f"bs={bs} part={part}")
+
+
+@pytest.mark.parametrize("bs", [8, 32])
+def test_decode_block_size_nan_slots_and_empty_context(bs):
+    """Unused slots and blocks hold NaN (they never leak); an empty context gives zeros."""
+    case = make_decode_case([65, bs], "bf16", [0, 3, 9, 41, 0, 100], 32, 8, 128)
+    p = reblock(case.paged, bs, np.random.default_rng(bs))
+    assert torch.isnan(p.pool.key_cache).any()
+    out = decode_on(p, case)
+    assert torch.all(out[0] == 0) and torch.all(out[4] == 0)
+    assert torch.isfinite(out).all()
+    check_close(out, oracle_on(p, case), "bf16", f"bs={bs} nan")
+
+
+def run_chunked_on(paged, case):
+    bs = paged.pool.block_size
+    say(f"chunked bs={bs} {case.dtype} q_lens={np.diff(case.cu_q_lens).tolist()} "
+        f"ctx={paged.context_lens.tolist()} Hq={case.num_q_heads} Hkv={case.num_kv_heads} D={case.head_dim}")
+    kc, vc = dev(paged.pool.key_cache), dev(paged.pool.value_cache)
+    pend = np.nonzero(paged.pending)[0]
+    ti = torch.from_numpy(pend)
+    pkv.reshape_and_cache(dev(paged.logical_k[ti].contiguous()), dev(paged.logical_v[ti].contiguous()), kc, vc,
+                          dev(paged.token_slots[pend].copy()))
+    q = dev(case.query)
+    out = torch.full_like(q, float("nan"))
+    pkv.paged_attention_chunked(out, q, dev(case.cu_q_lens), case.max_q_len, kc, vc, dev(paged.block_tables),
+                                dev(paged.context_lens), case.scale)
+    torch.cuda.synchronize()
+    return out, kc, vc
+
+
+@pytest.mark.parametrize("bs", [8, 32])
+@pytest.mark.parametrize("dtype,G,Hkv,D,cached,q_lens", [
+    ("bf16", 1, 2, 128, [0, 5, 40], [7, 16, 33]),
+    ("f16", 4, 2, 64, [100, 0], [1, 50]),
+    ("bf16", 4, 2, 128, [1000, 37], [200, 95]),
+    ("bf16", 32, 1, 128, [200, 31], [40, 17]),
+])
+def test_chunked_block_size_matches_oracle_and_bs16(bs, dtype, G, Hkv, D, cached, q_lens):
+    case = make_chunked_case([66, G, D], dtype, cached, q_lens, G * Hkv, Hkv, D)
+    p = reblock(case.paged, bs, np.random.default_rng([67, bs]))
+    out, kc, vc = run_chunked_on(p, case)
+    pool = p.pool.clone()
+    pend = np.nonzero(p.pending)[0]
+    ti = torch.from_numpy(pend)
+    oracle.reshape_and_cache(p.logical_k[ti], p.logical_v[ti], pool.key_cache, pool.value_cache,
+                             p.token_slots[pend], dtype)
+    ref = oracle.chunked(case.query, case.cu_q_lens, pool.key_cache, pool.value_cache, p.block_tables,
+                         p.context_lens, Hkv, bs, case.scale, dtype)
+    check_close(out, ref, dtype, f"chunked bs={bs}")
+    assert torch.equal(bits(kc.cpu()), bits(pool.key_cache))
+    assert torch.equal(bits(vc.cpu()), bits(pool.value_cache))
+    out16, _, _ = run_chunked_on(case.paged, case)
+    assert torch.equal(bits(out), bits(out16)), f"chunked bs={bs} vs 16"
+
+
+@pytest.mark.parametrize("bs", [8, 32])
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_reshape_and_cache_block_size_bit_exact(bs, dtype):
+    say(f"reshape_and_cache bs={bs} {dtype}")
+    rng = np.random.default_rng([68, bs])
+    NB, H, D, n = 64, 4, 128, 250
+    pool = new_pool(dtype, NB, H, D, bs)
+    pool.key_cache[:5] = torch.from_numpy(rng.standard_normal((5, H, bs, D), dtype=np.float32)).to(
+        pool.key_cache.dtype)
+    slots = rng.choice(NB * bs, size=n, replace=False).astype(np.int64)
+    slots[::13] = -1
+    k = torch.from_numpy(rng.standard_normal((n, H, D), dtype=np.float32)).to(DTYPES[dtype][0])
+    v = torch.from_numpy(rng.standard_normal((n, H, D), dtype=np.float32)).to(DTYPES[dtype][0])
+    kc, vc = dev(pool.key_cache), dev(pool.value_cache)
+    pkv.reshape_and_cache(dev(k), dev(v), kc, vc, dev(slots))
+    torch.cuda.synchronize()
+    oracle.reshape_and_cache(k, v, pool.key_cache, pool.value_cache, slots, dtype)
+    assert torch.equal(bits(kc.cpu()), bits(pool.key_cache))
+    assert torch.equal(bits(vc.cpu()), bits(pool.value_cache))
+
+
+@pytest.mark.parametrize("bs", [8, 32])
+def test_copy_blocks_block_size_bit_exact(bs):
+    say(f"copy_blocks bs={bs}")
+    rng = np.random.default_rng([69, bs])
+    L, NB, H, D = 2, 48, 8, 128
+    ks = [torch.from_numpy(rng.standard_normal((NB, H, bs, D), dtype=np.float32)).to(torch.bfloat16)
+          for _ in range(L)]
+    vs = [torch.from_numpy(rng.standard_normal((NB, H, D, bs), dtype=np.float32)).to(torch.bfloat16)
+          for _ in range(L)]
+    perm = rng.permutation(NB)
+    pairs = np.stack([perm[:15], perm[15:30]], axis=1).astype(np.int64)
+    kd = [dev(x) for x in ks]
+    vd = [dev(x) for x in vs]
+    pkv.copy_blocks(kd, vd, dev(pairs))
+    torch.cuda.synchronize()
+    oracle.copy_blocks(ks, vs, pairs, "bf16")
+    for layer in range(L):
+        assert torch.equal(bits(kd[layer].cpu()), bits(ks[layer]))
+        assert torch.equal(bits(vd[layer].cpu()), bits(vs[layer]))

@@ -17,7 +17,8 @@ import torch
 import oracle
 from oracle import brute
 import workloads
-from workloads.gen import INT32_MAX, build_paged, make_cow_case, make_decode_case, new_pool, write_tokens
+from workloads.gen import (INT32_MAX, build_paged, make_chunked_case, make_cow_case, make_decode_case, new_pool,
+                           reblock, write_tokens)
 
 GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
 
@@ -148,6 +149,43 @@ def test_placement_invariance_bitwise(dtype):
         k, v, bt = _replace(case, np.random.default_rng(seed))
         b = oracle.decode(case.query, k, v, bt, case.context_lens, 2, 16, case.scale, dtype)
         assert np.array_equal(a, b)
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("bs", [8, 32])
+def test_block_size_invariance(dtype, bs):
+    """Page 1, paging section: a block is only the storage unit of the KV cache.  The
+    same tokens stored in blocks of 8, 16 or 32 give the same attention bit for bit
+    (the tokens are gathered back in logical order before any arithmetic), and that
+    attention is the dense one on the logical K/V."""
+    case = make_decode_case([3, 2], dtype, [1, 7, 8, 9, 16, 17, 31, 33, 100], 8, 2, 64)
+    a = _dec(case)
+    p = reblock(case.paged, bs, np.random.default_rng(bs))
+    assert p.pool.key_cache.shape[2] == bs and p.pool.value_cache.shape[3] == bs
+    b = oracle.decode(case.query, p.pool.key_cache, p.pool.value_cache, p.block_tables, p.context_lens, 2, bs,
+                      case.scale, dtype)
+    assert np.array_equal(a, b)
+    ref = brute.decode(case.query, p.logical_k, p.logical_v, p.cu_tokens, case.scale)
+    np.testing.assert_allclose(b, ref.reshape(b.shape), rtol=1e-12, atol=1e-12)
+
+
+@pytest.mark.parametrize("bs", [8, 32])
+def test_chunked_block_size_invariance(bs):
+    """The chunked rows are the same for every block size of the pool."""
+    case = make_chunked_case([5, bs], "bf16", [0, 9, 40], [7, 16, 33], 4, 2, 64)
+    pool = case.paged.pool.clone()
+    oracle.reshape_and_cache(case.new_key, case.new_value, pool.key_cache, pool.value_cache, case.slot_mapping,
+                             "bf16")
+    a = oracle.chunked(case.query, case.cu_q_lens, pool.key_cache, pool.value_cache, case.paged.block_tables,
+                       case.paged.context_lens, 2, 16, case.scale, "bf16")
+    p = reblock(case.paged, bs, np.random.default_rng(bs))
+    # the chunk's own tokens go in through the cache write, at their slots in the new layout
+    pend = np.nonzero(p.pending)[0]
+    oracle.reshape_and_cache(p.logical_k[torch.from_numpy(pend)], p.logical_v[torch.from_numpy(pend)],
+                             p.pool.key_cache, p.pool.value_cache, p.token_slots[pend], "bf16")
+    b = oracle.chunked(case.query, case.cu_q_lens, p.pool.key_cache, p.pool.value_cache, p.block_tables,
+                       p.context_lens, 2, bs, case.scale, "bf16")
+    assert np.array_equal(a, b)
 
 
 def test_ctx_one_is_first_value_exactly():

@@ -107,8 +107,23 @@ def build_paged(rng: np.random.Generator, dtype: str, num_kv_heads: int, head_di
     Sequence s has context_lens[s] tokens; the first resident_lens[s] are written
     now, the rest are marked pending (their slots stay NaN)."""
     ctx = np.asarray(context_lens, dtype=np.int64)
-    S = len(ctx)
     res = ctx if resident_lens is None else np.asarray(resident_lens, dtype=np.int64)
+    NB, bt, cu, slots = _place(rng, ctx, block_size, max_blocks_per_seq, num_blocks, pool_factor)
+    T = int(cu[-1])
+    pend = np.zeros(T, dtype=bool)
+    for s in range(len(ctx)):
+        pend[cu[s]:cu[s + 1]] = np.arange(int(ctx[s])) >= res[s]
+    k = _cast(rng.standard_normal((T, num_kv_heads, head_dim), dtype=np.float32), dtype)
+    v = _cast(rng.standard_normal((T, num_kv_heads, head_dim), dtype=np.float32), dtype)
+    pool = new_pool(dtype, NB, num_kv_heads, head_dim, block_size)
+    keep = ~pend
+    write_tokens(pool, slots[keep], k[torch.from_numpy(keep)], v[torch.from_numpy(keep)])
+    return Paged(pool, ctx.astype(np.int32), bt, cu, k, v, slots, pend)
+
+
+def _place(rng, ctx, block_size, max_blocks_per_seq, num_blocks, pool_factor):
+    """Random block placement: (pool blocks, block tables, token offsets, token slots)."""
+    S = len(ctx)
     nblk = (ctx + block_size - 1) // block_size
     need = int(nblk.sum())
     MB = int(max(1, nblk.max() if S else 1)) if max_blocks_per_seq is None else int(max_blocks_per_seq)
@@ -119,9 +134,7 @@ def build_paged(rng: np.random.Generator, dtype: str, num_kv_heads: int, head_di
     bt = np.full((S, MB), INT32_MAX, dtype=np.int32)
     cu = np.zeros(S + 1, dtype=np.int64)
     cu[1:] = np.cumsum(ctx)
-    T = int(cu[-1])
-    slots = np.empty(T, dtype=np.int64)
-    pend = np.zeros(T, dtype=bool)
+    slots = np.empty(int(cu[-1]), dtype=np.int64)
     pos = 0
     for s in range(S):
         n = int(ctx[s])
@@ -131,13 +144,20 @@ def build_paged(rng: np.random.Generator, dtype: str, num_kv_heads: int, head_di
         bt[s, :b] = phys
         t = np.arange(n, dtype=np.int64)
         slots[cu[s]:cu[s + 1]] = phys[t // block_size].astype(np.int64) * block_size + t % block_size
-        pend[cu[s]:cu[s + 1]] = t >= res[s]
-    k = _cast(rng.standard_normal((T, num_kv_heads, head_dim), dtype=np.float32), dtype)
-    v = _cast(rng.standard_normal((T, num_kv_heads, head_dim), dtype=np.float32), dtype)
-    pool = new_pool(dtype, NB, num_kv_heads, head_dim, block_size)
-    keep = ~pend
-    write_tokens(pool, slots[keep], k[torch.from_numpy(keep)], v[torch.from_numpy(keep)])
-    return Paged(pool, ctx.astype(np.int32), bt, cu, k, v, slots, pend)
+    return NB, bt, cu, slots
+
+
+def reblock(p: Paged, block_size: int, rng: np.random.Generator, pool_factor: float = 1.25) -> Paged:
+    """The same logical K/V (pending tokens stay unwritten) in a new pool of another
+    block size, with a fresh random placement."""
+    ctx = p.context_lens.astype(np.int64)
+    nblk = (ctx + block_size - 1) // block_size
+    NB, bt, cu, slots = _place(rng, ctx, block_size, None, None, pool_factor)
+    pool = new_pool(p.pool.dtype, NB, p.pool.num_kv_heads, p.pool.head_dim, block_size)
+    keep = ~p.pending
+    write_tokens(pool, slots[keep], p.logical_k[torch.from_numpy(keep)], p.logical_v[torch.from_numpy(keep)])
+    assert bt.shape[1] == max(1, int(nblk.max() if len(ctx) else 1))
+    return Paged(pool, p.context_lens.copy(), bt, cu, p.logical_k, p.logical_v, slots, p.pending.copy())
 
 
 @dataclass
