@@ -176,7 +176,7 @@ def main():
     ap.add_argument("--partition-size", type=int, default=None)
     ap.add_argument("--paging-study", action="store_true",
                     help="time the decode call on the same batch with shuffled and with contiguous block "
-                         "placement, in one process, and print both")
+                         "placement, and with blocks of 8 and 32 tokens, in one process, and print all")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="time a plain 1 GiB device copy (reference kernel for the HBM counters)")
@@ -372,30 +372,63 @@ def run_long(args, p, qd, qc, cu, torch, pkv, workloads, dev):
 
 def paging_study(args, torch, pkv, workloads, dev, case, kc, vc, q, bt, cl, new, part, ws):
     """The pages report the paged kernel 20-26 % slower than a contiguous one on
-    their GPU ([P1] paging section).  Here: the same batch, the same kernel, with
-    the generator's shuffled block placement and with every sequence's blocks laid
-    out contiguously in logical order (identity placement), timed alternately."""
+    their GPU, and weigh the block size: small blocks waste fewer slots in each
+    sequence's last block but need longer tables ([P1] paging section).  Here: the
+    same batch and kernel with the generator's shuffled placement, with every
+    sequence's blocks laid out contiguously in logical order (identity placement),
+    and with the same tokens re-laid in shuffled pools of 8- and 32-token blocks;
+    all timed alternately.  The re-layout is plain tensor indexing on the GPU."""
     if new is not None:
         pkv.reshape_and_cache(new[0], new[1], kc, vc, new[2])
-    nb = (case.context_lens.astype(np.int64) + 15) // 16
-    order = np.concatenate([case.block_tables[s, :nb[s]] for s in range(case.num_seqs)]).astype(np.int64)
+    S = case.num_seqs
+    ctx = case.context_lens.astype(np.int64)
+    nb = (ctx + 15) // 16
+    order = np.concatenate([case.block_tables[s, :nb[s]] for s in range(S)]).astype(np.int64)
     new_id = np.arange(len(order), dtype=np.int32)
     bt_id = np.full_like(case.block_tables, 0x7FFFFFFF)
     pos = 0
-    for s in range(case.num_seqs):
+    for s in range(S):
         bt_id[s, :nb[s]] = new_id[pos:pos + nb[s]]
         pos += nb[s]
     idx = torch.from_numpy(order).to(dev)
     kc_id, vc_id = kc[idx].contiguous(), vc[idx].contiguous()
     bt_id_d = torch.from_numpy(bt_id).to(dev)
-    out = torch.empty_like(q)
     layouts = {"shuffled": (kc, vc, bt), "contiguous": (kc_id, vc_id, bt_id_d)}
-    times = {k: [] for k in layouts}
+
+    # every token of the batch, gathered from the 16-token pool: [T, Hkv, D]
+    seq_of = np.repeat(np.arange(S), ctx)
+    tok = np.arange(int(ctx.sum()), dtype=np.int64) - np.repeat(np.concatenate([[0], np.cumsum(ctx)[:-1]]), ctx)
+    p16 = torch.from_numpy(case.block_tables[seq_of, tok // 16].astype(np.int64)).to(dev)
+    o16 = torch.from_numpy(tok % 16).to(dev)
+    k_log, v_log = kc[p16, :, o16, :], vc[p16, :, :, o16]
+    rng = np.random.default_rng(265)
+    geometry = {16: (int(nb.sum()), int((nb * 16).sum()))}
+    for bs in (8, 32):
+        nbb = (ctx + bs - 1) // bs
+        need = int(nbb.sum())
+        perm = rng.permutation(need).astype(np.int32)
+        btb = np.full((S, int(nbb.max())), 0x7FFFFFFF, dtype=np.int32)
+        first = np.concatenate([[0], np.cumsum(nbb)[:-1]])
+        for s in range(S):
+            btb[s, :nbb[s]] = perm[first[s]:first[s] + nbb[s]]
+        pb = torch.from_numpy(btb[seq_of, tok // bs].astype(np.int64)).to(dev)
+        ob = torch.from_numpy(tok % bs).to(dev)
+        kb = torch.full((need, case.num_kv_heads, bs, case.head_dim), float("nan"), dtype=kc.dtype, device=dev)
+        vb = torch.full((need, case.num_kv_heads, case.head_dim, bs), float("nan"), dtype=vc.dtype, device=dev)
+        kb[pb, :, ob, :] = k_log
+        vb[pb, :, :, ob] = v_log
+        layouts[f"block_size_{bs}"] = (kb, vb, torch.from_numpy(btb).to(dev))
+        geometry[bs] = (need, int((nbb * bs).sum()))
+    del k_log, v_log, p16, o16
+
+    outs, times = {}, {k: [] for k in layouts}
     for rep in range(6):
         for name, (k_, v_, b_) in layouts.items():
+            out = torch.empty_like(q)
             for _ in range(3):
                 pkv.paged_attention_decode(out, q, k_, v_, b_, cl, case.scale, partition_size=part, workspace=ws)
             torch.cuda.synchronize()
+            outs[name] = out
             e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
             e0.record()
             for _ in range(args.steps):
@@ -406,9 +439,19 @@ def paging_study(args, torch, pkv, workloads, dev, case, kc, vc, q, bt, cl, new,
     nbytes = workloads.algorithmic_decode_bytes(case.context_lens, case.num_q_heads, case.num_kv_heads,
                                                 case.head_dim, workloads.DTYPES[case.dtype][2])
     med = {k: float(np.median(v)) for k, v in times.items()}
-    print(json.dumps({"paging_study": args.workload, "call_ms_median": {k: round(v, 4) for k, v in med.items()},
-                      "GBs": {k: round(nbytes / (v * 1e-3) / 1e9, 1) for k, v in med.items()},
-                      "paged_over_contiguous": round(med["shuffled"] / med["contiguous"], 4)}), flush=True)
+    used = int(ctx.sum())
+    print(json.dumps({
+        "paging_study": args.workload,
+        "call_ms_median": {k: round(v, 4) for k, v in med.items()},
+        "GBs": {k: round(nbytes / (v * 1e-3) / 1e9, 1) for k, v in med.items()},
+        "paged_over_contiguous": round(med["shuffled"] / med["contiguous"], 4),
+        "block_size": {str(bs): {"table_entries": g[0], "slots_allocated": g[1],
+                                 "unused_slot_fraction": round(1 - used / g[1], 5),
+                                 "call_ms": round(med["shuffled" if bs == 16 else f"block_size_{bs}"], 4)}
+                       for bs, g in sorted(geometry.items())},
+        "same_bits_as_block_size_16": {k: bool(torch.equal(outs[k].view(torch.int16), outs["shuffled"].view(
+            torch.int16))) for k in outs if k.startswith("block_size")},
+    }), flush=True)
 
 
 def run_cow(args, torch, pkv, workloads, dev):

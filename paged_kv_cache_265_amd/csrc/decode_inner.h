@@ -13,6 +13,12 @@
 
 namespace pkv {
 
+// Cache policy of the V loads: a tile of a 32-token block reads half of every
+// head_dim row of the block's V tile, and the block's other tile -- folded next by
+// the same wave -- reads the other half of the same cache lines, so those loads keep
+// the default policy; everything else streams.
+template <int BS> constexpr int kVPolicy = BS == 32 ? 0 : kNonTemporal;
+
 // Where the 16 tokens of one tile of a (sequence, kv head) are.  Units are
 // (physical block * Hkv + kv head), i.e. (block, kv head) tiles of the pools, each
 // BS * D elements (K: [BS][D] token-major; V: [D][BS] head_dim-major).
@@ -119,7 +125,7 @@ struct MfmaLoop {
 #pragma unroll
             for (int ks = 0; ks < KS; ++ks) t.k[ks] = stream_load16(kr, koff + ks * 64);
 #pragma unroll
-            for (int dt = 0; dt < DT; ++dt) t.v[dt] = stream_load8(vr, voff + dt * 16 * BS * 2);
+            for (int dt = 0; dt < DT; ++dt) t.v[dt] = policy_load8<kVPolicy<BS>>(vr, voff + dt * 16 * BS * 2);
         }
     }
 
@@ -311,7 +317,7 @@ struct MfmaWideLoop {
 #pragma unroll
             for (int ks = 0; ks < KS; ++ks) t.k[ks] = stream_load16(kr, koff + ks * 64);
 #pragma unroll
-            for (int dq = 0; dq < DQ; ++dq) t.v[dq] = stream_load16(vr, voff + dq * 32 * BS * 2);
+            for (int dq = 0; dq < DQ; ++dq) t.v[dq] = policy_load16<kVPolicy<BS>>(vr, voff + dq * 32 * BS * 2);
         }
     }
 
@@ -542,7 +548,7 @@ struct ValuLoop {
 #pragma unroll
             for (int k = 0; k < KC; ++k) t.k[k] = stream_load16(kr, kt + (sub + 4 * k) * 16);
 #pragma unroll
-            for (int c = 0; c < VC; ++c) t.v[c] = stream_load16(vr, vt + c * kRowStep);
+            for (int c = 0; c < VC; ++c) t.v[c] = policy_load16<kVPolicy<BS>>(vr, vt + c * kRowStep);
         }
     }
 

@@ -153,6 +153,16 @@ __device__ __forceinline__ uint2 stream_load8(rsrc_t r, uint32_t off) {
     const u32x2 x = __builtin_amdgcn_raw_buffer_load_b64(r, (int)off, 0, kNonTemporal);
     return make_uint2(x.x, x.y);
 }
+// The same with a choice of cache policy: kAux = kNonTemporal streams, 0 keeps the
+// default policy (for lines whose other half another load reads soon after).
+template <int kAux> __device__ __forceinline__ uint4 policy_load16(rsrc_t r, uint32_t off) {
+    const u32x4 x = __builtin_amdgcn_raw_buffer_load_b128(r, (int)off, 0, kAux);
+    return make_uint4(x.x, x.y, x.z, x.w);
+}
+template <int kAux> __device__ __forceinline__ uint2 policy_load8(rsrc_t r, uint32_t off) {
+    const u32x2 x = __builtin_amdgcn_raw_buffer_load_b64(r, (int)off, 0, kAux);
+    return make_uint2(x.x, x.y);
+}
 
 // ---- misc ------------------------------------------------------------------------------
 
