@@ -372,17 +372,15 @@ __global__ __launch_bounds__(256) void decode_merge_stream(DecodeParams p, int s
 // Pieces: the fixed partitions 0 .. nparts-1 of the stream, or, for the balanced
 // split, the waves w0 .. w1 whose unit ranges cut the stream (w0's last record,
 // then slot 0 of the others; when U < N each unit sits alone in its own wave).
-// 256 threads = 2 groups x 128 head_dim lanes; group g folds pieces g, g+2, ...
-// with the weights 2^(m_i - M) taken from LDS.  Balanced split only: sequences
-// with an empty context get their zero output here.
+// 256 threads = 2 groups x 128 head_dim lanes; group g folds pieces g, g+2, ... in
+// one online pass, kChunk pieces at a time with all their loads in flight, (M, L, O)
+// rescaled by 2^(M_old - M_new); the two groups are joined through LDS at the end.
+// Balanced split only: sequences with an empty context get their zero output here.
 // ---------------------------------------------------------------------------------------
 template <int K, int HT>
 __global__ __launch_bounds__(256) void decode_merge_head(DecodeParams p, int split_waves) {
-    constexpr int kRound = 1024;  // pieces folded per round
-    __shared__ const float* ptr[kRound];
-    __shared__ float wts[kRound];
-    __shared__ float red[8];
-    __shared__ float part_o[128];
+    constexpr int kChunk = 16;  // pieces per group in flight at once
+    __shared__ float other[128 + 2];
     const int NS = p.Hkv * p.chunks;
     const int cap = min(p.G, HT);
     int idx = blockIdx.x;
@@ -395,7 +393,7 @@ __global__ __launch_bounds__(256) void decode_merge_head(DecodeParams p, int spl
     const int ctx = p.context_lens[s];
     const int D = p.D;
     const size_t rec = (size_t)cap * (D + 2);
-    const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+    const int tid = threadIdx.x;
 
     long long count, w0 = 0, U = 0, a = 0;
     const long long N = split_waves;
@@ -423,39 +421,55 @@ __global__ __launch_bounds__(256) void decode_merge_head(DecodeParams p, int spl
         if (i == 0) return first;
         return p.ws + (size_t)(U >= N ? w0 + i : wave_of(a + i, U, N)) * 2 * rec;
     };
-    float M = kNegInf;
-    for (long long i = tid; i < count; i += 256) M = fmaxf(M, record(i)[cap * D + h]);
-#pragma unroll
-    for (int m = 1; m < 64; m <<= 1) M = fmaxf(M, __shfl_xor(M, m, 64));
-    if (lane == 0) red[wv] = M;
-    __syncthreads();
-    M = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
-    float L = 0.f, O = 0.f;
     const int g = tid >> 7, d = tid & 127;
-    for (long long r0 = 0; r0 < count; r0 += kRound) {
-        const int n = (int)min((long long)kRound, count - r0);
-        __syncthreads();
-        for (int i = tid; i < n; i += 256) {
-            const float* r = record(r0 + i);
-            const float w = fast_exp2(r[cap * D + h] - M);
-            ptr[i] = r;
-            wts[i] = w;
-            L += w * r[cap * D + cap + h];
+    const int dd = d < D ? d : 0;  // lanes past head_dim read element 0 and store nothing
+    float M = kNegInf, L = 0.f, O = 0.f;
+    for (long long i0 = g; i0 < count; i0 += 2 * kChunk) {
+        float mv[kChunk], lv[kChunk], av[kChunk];
+#pragma unroll
+        for (int j = 0; j < kChunk; ++j) {
+            mv[j] = kNegInf;
+            lv[j] = av[j] = 0.f;
+            const long long i = i0 + 2 * j;
+            if (i < count) {
+                const float* r = record(i);
+                mv[j] = r[cap * D + h];
+                lv[j] = r[cap * D + cap + h];
+                av[j] = r[h * D + dd];
+            }
         }
-        __syncthreads();
-        if (d < D) {
-#pragma unroll 16
-            for (int i = g; i < n; i += 2) O += wts[i] * ptr[i][h * D + d];
+        float mn = M;
+#pragma unroll
+        for (int j = 0; j < kChunk; ++j) mn = fmaxf(mn, mv[j]);
+        const float sc = fast_exp2(M - mn);  // M = -inf on the first chunk: sc = 0 and L = O = 0 anyway
+        L *= sc;
+        O *= sc;
+#pragma unroll
+        for (int j = 0; j < kChunk; ++j) {
+            const float wt = fast_exp2(mv[j] - mn);
+            L += wt * lv[j];
+            O += wt * av[j];
+        }
+        M = mn;
+    }
+    // join group 1 into group 0 (every piece has a finite m, so both M are finite
+    // whenever the group had a piece; a group without pieces keeps M = -inf, L = O = 0)
+    if (g == 1) {
+        other[d] = O;
+        if (d == 0) {
+            other[128] = M;
+            other[129] = L;
         }
     }
-#pragma unroll
-    for (int m = 1; m < 64; m <<= 1) L += __shfl_xor(L, m, 64);
-    if (lane == 0) red[4 + wv] = L;
-    if (g == 1) part_o[d] = O;
     __syncthreads();
-    L = red[4] + red[5] + red[6] + red[7];
-    if (g == 0 && d < D)
-        store_elem<K>(p.out, ((size_t)s * p.Hq + hd.head0 + h) * D + d, L > 0.f ? (O + part_o[d]) / L : 0.f);
+    if (g == 0 && d < D) {
+        const float M1 = other[128], L1 = other[129], O1 = other[d];
+        const float mn = fmaxf(M, M1);
+        const float s0 = M == kNegInf ? 0.f : fast_exp2(M - mn);
+        const float s1 = M1 == kNegInf ? 0.f : fast_exp2(M1 - mn);
+        const float Lt = L * s0 + L1 * s1;
+        store_elem<K>(p.out, ((size_t)s * p.Hq + hd.head0 + h) * D + d, Lt > 0.f ? (O * s0 + O1 * s1) / Lt : 0.f);
+    }
 }
 
 // ---------------------------------------------------------------------------------------
