@@ -352,6 +352,38 @@ def run_long(args, p, qd, qc, cu, torch, pkv, workloads, dev):
     e1.record()
     torch.cuda.synchronize()
     fix_ms = e0.elapsed_time(e1) / args.steps
+    # the whole flattened batch in one attention launch: decode tokens as one-row
+    # segments beside the prefill chunks, against the two calls back to back
+    cum = np.concatenate([np.arange(S + 1), S + cu[1:]]).astype(np.int32)
+    cumd = torch.from_numpy(cum).to(dev)
+    qm = torch.cat([q, qcd]).contiguous()
+    outm = torch.empty_like(qm)
+    wsm = torch.empty(pkv.mixed_workspace_size(len(cum) - 1, 32, 1, 128, 16), dtype=torch.uint8, device=dev)
+
+    def mixed():
+        pkv.paged_attention_mixed(outm, qm, cumd, 512, kc, vc, bt, cl, scale, workspace=wsm)
+
+    def separate():
+        pkv.paged_attention_decode(out, q, kc, vc, bt[:S], cl[:S], scale, partition_size=0, workspace=ws)
+        pkv.paged_attention_chunked(outc, qcd, cud, 512, kc, vc, bt[S:], cl[S:], scale)
+
+    times = {"mixed": [], "separate": []}
+    for rep in range(4):
+        for name, fn in (("mixed", mixed), ("separate", separate)):
+            for _ in range(2):
+                fn()
+            torch.cuda.synchronize()
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            for _ in range(args.steps):
+                fn()
+            e1.record()
+            torch.cuda.synchronize()
+            times[name].append(e0.elapsed_time(e1) / args.steps)
+    mix_ms, sep_ms = float(np.median(times["mixed"])), float(np.median(times["separate"]))
+    mixed_vs_separate = {
+        "decode_rows_max_abs_diff": float((outm[:S].float() - out.float()).abs().max()),
+        "prefill_rows_max_abs_diff": float((outm[S:].float() - outc.float()).abs().max())}
     nbytes = workloads.algorithmic_decode_bytes(p.context_lens[:S], 32, 1, 128, 2)
     flops = workloads.algorithmic_chunked_flops(p.context_lens[S:], np.diff(cu), 32, 128)
     res = {"metric": METRIC, "value": round(nbytes / (dec_ms * 1e-3) / 1e9, 1), "unit": "GB/s", "n_gpus": 1,
@@ -364,6 +396,8 @@ def run_long(args, p, qd, qc, cu, torch, pkv, workloads, dev):
            "decode_partition512_ms": round(fix_ms, 4),
            "decode_partition512_GBs": round(nbytes / (fix_ms * 1e-3) / 1e9, 1),
            "chunked_tflops": round(flops / (chk_ms * 1e-3) / 1e12, 2),
+           "mixed_single_launch_ms": round(mix_ms, 4), "separate_calls_ms": round(sep_ms, 4),
+           "mixed_speedup": round(sep_ms / mix_ms, 4), "mixed_vs_separate": mixed_vs_separate,
            "roofline": {"bound": "hbm", "kernel": "paged_attention_decode", "achieved":
                         round(nbytes / (dec_ms * 1e-3) / 1e9, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
                         "frac": round(nbytes / (dec_ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4), "traffic": None}}

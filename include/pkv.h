@@ -6,6 +6,8 @@
  *   paged_attention_chunked  causal attention of short query chunks (chunked prefill)
  *   reshape_and_cache        write new K/V tokens into their slots
  *   copy_blocks              whole-block copies for copy-on-write
+ * and paged_attention_mixed runs a flattened batch of decode tokens and prefill
+ * chunks (the chunked call's arguments) in one attention launch.
  *
  * Sources.  The operation is the one described on three web pages:
  *  [P1] "每生成一个字都要把全部权重读一遍：从 vLLM 看 LLM 推理提速" -- section on paging
@@ -161,6 +163,32 @@ int paged_attention_chunked(void* out, const void* query, const int32_t* cu_q_le
                             const int32_t* block_tables, const int32_t* context_lens, int num_q_heads,
                             int num_kv_heads, int head_dim, int block_size, int num_blocks, int max_blocks_per_seq,
                             float scale, int dtype, void* stream);
+
+/*
+ * paged_attention_mixed -- [P2] sections 1.4 and 2.1: one pass over a flattened
+ * batch that mixes prefill chunks and decode tokens.
+ *
+ * Computes exactly what paged_attention_chunked computes for the same arguments
+ * (every segment, causal rows), in one attention launch plus a small merge
+ * launch: segments with one query row are decode sequences, whose contexts are
+ * cut across many waves (the balanced split of paged_attention_decode) and merged;
+ * the other segments run as chunked-prefill tiles beside them, so the HBM-bound
+ * decode and the matrix-core-bound prefill overlap.  16-bit types only.
+ *   workspace / workspace_bytes: device buffer of at least
+ *   pkv_mixed_workspace_size(...) bytes, 16-byte aligned; contents on entry do
+ *   not matter.  Calls that share a workspace must not overlap in time.
+ * Requires context_lens[i] >= L_i (device contract).  Deterministic bit for bit on
+ * repeat; decode rows agree with paged_attention_decode to fp32 rounding order.
+ */
+int paged_attention_mixed(void* out, const void* query, const int32_t* cu_q_lens, int num_segs, int total_q,
+                          int max_q_len, const void* key_cache, const void* value_cache, const int32_t* block_tables,
+                          const int32_t* context_lens, int num_q_heads, int num_kv_heads, int head_dim,
+                          int block_size, int num_blocks, int max_blocks_per_seq, float scale, int dtype,
+                          void* workspace, size_t workspace_bytes, void* stream);
+
+/* Bytes of workspace paged_attention_mixed needs (the balanced-split workspace of
+ * paged_attention_decode for num_segs sequences); 0 on invalid arguments. */
+size_t pkv_mixed_workspace_size(int num_segs, int num_q_heads, int num_kv_heads, int head_dim, int block_size);
 
 /*
  * reshape_and_cache -- [P2] section 1.6 (slot_mapping); [P3] section 3.1 (append the

@@ -11,8 +11,10 @@ from .pkv import (  # noqa: F401
     decode_partition_size,
     decode_workspace_size,
     load_library,
+    mixed_workspace_size,
     paged_attention_chunked,
     paged_attention_decode,
+    paged_attention_mixed,
     read_probe,
     reshape_and_cache,
     version,

@@ -193,6 +193,7 @@ int paged_attention_decode(void* out, const void* query, const void* key_cache, 
     p.vc = value_cache;
     p.block_tables = block_tables;
     p.context_lens = context_lens;
+    p.cu_q = nullptr;
     if (partition_size == 0) {
         p.starts = (long long*)workspace;
         p.ws = (float*)((char*)workspace + split_prefix_bytes(num_seqs));
@@ -264,6 +265,92 @@ int paged_attention_chunked(void* out, const void* query, const int32_t* cu_q_le
     p.max_q_len = max_q_len;
     p.scale_log2 = scale * pkv::kLog2eHost;
     hipError_t e = pkv::launch_chunked(p, dtype, (hipStream_t)stream);
+    if (e != hipSuccess) return hip_fail(e, fn);
+    return PKV_OK;
+}
+
+size_t pkv_mixed_workspace_size(int num_segs, int num_q_heads, int num_kv_heads, int head_dim, int block_size) {
+    if (num_segs <= 0) return 0;
+    return pkv_decode_workspace_size(num_segs, num_q_heads, num_kv_heads, head_dim, block_size, 1, 0);
+}
+
+int paged_attention_mixed(void* out, const void* query, const int32_t* cu_q_lens, int num_segs, int total_q,
+                          int max_q_len, const void* key_cache, const void* value_cache, const int32_t* block_tables,
+                          const int32_t* context_lens, int num_q_heads, int num_kv_heads, int head_dim,
+                          int block_size, int num_blocks, int max_blocks_per_seq, float scale, int dtype,
+                          void* workspace, size_t workspace_bytes, void* stream) {
+    static const char* fn = "paged_attention_mixed";
+    int rc;
+    if ((rc = check_pool(fn, num_kv_heads, head_dim, block_size, num_blocks, dtype)) != PKV_OK) return rc;
+    if ((rc = check_heads(fn, num_q_heads, num_kv_heads)) != PKV_OK) return rc;
+    if (dtype == PKV_F32) return set_error(PKV_ERR_UNSUPPORTED, "%s: fp32 is not supported (16-bit types only)", fn);
+    if (num_segs < 0 || total_q < 0 || max_q_len < 0)
+        return set_error(PKV_ERR_INVALID, "%s: num_segs, total_q and max_q_len must be >= 0", fn);
+    if (max_blocks_per_seq <= 0)
+        return set_error(PKV_ERR_INVALID, "%s: max_blocks_per_seq must be positive (got %d)", fn, max_blocks_per_seq);
+    if (!std::isfinite(scale) || !(scale > 0.f))
+        return set_error(PKV_ERR_INVALID, "%s: scale must be finite and positive", fn);
+    if (max_q_len > total_q) return set_error(PKV_ERR_INVALID, "%s: max_q_len exceeds total_q", fn);
+    if (num_segs == 0 || total_q == 0 || max_q_len == 0) return PKV_OK;
+    if (!out || !query || !cu_q_lens || !key_cache || !value_cache || !block_tables || !context_lens)
+        return set_error(PKV_ERR_INVALID, "%s: null pointer argument", fn);
+    if (!aligned(out, 16) || !aligned(query, 16) || !aligned(key_cache, 16) || !aligned(value_cache, 16) ||
+        !aligned(block_tables, 4) || !aligned(context_lens, 4) || !aligned(cu_q_lens, 4))
+        return set_error(PKV_ERR_INVALID, "%s: misaligned pointer", fn);
+    const int G = num_q_heads / num_kv_heads;
+    const long long tiles = ((long long)max_q_len * G + 127) / 128;
+    if (tiles * num_kv_heads * num_segs + 8192 > 0x7fffffffLL ||
+        (long long)num_segs * num_q_heads > 0x7fffffffLL)
+        return set_error(PKV_ERR_INVALID, "%s: problem too large for one launch", fn);
+    const size_t need = pkv_mixed_workspace_size(num_segs, num_q_heads, num_kv_heads, head_dim, block_size);
+    if (!workspace || workspace_bytes < need)
+        return set_error(PKV_ERR_WORKSPACE, "%s: workspace of %zu bytes needed, %zu given", fn, need,
+                         workspace ? workspace_bytes : (size_t)0);
+    if (!aligned(workspace, 16)) return set_error(PKV_ERR_INVALID, "%s: workspace must be 16-byte aligned", fn);
+
+    pkv::ChunkedParams c;
+    c.out = out;
+    c.q = query;
+    c.cu_q_lens = cu_q_lens;
+    c.kc = key_cache;
+    c.vc = value_cache;
+    c.block_tables = block_tables;
+    c.context_lens = context_lens;
+    c.num_segs = num_segs;
+    c.Hq = num_q_heads;
+    c.Hkv = num_kv_heads;
+    c.G = G;
+    c.D = head_dim;
+    c.NB = num_blocks;
+    c.MB = max_blocks_per_seq;
+    c.BS = block_size;
+    c.head_chunk = G;
+    c.max_q_len = max_q_len;
+    c.scale_log2 = scale * pkv::kLog2eHost;
+
+    pkv::DecodeParams d;
+    d.out = out;
+    d.q = query;
+    d.kc = key_cache;
+    d.vc = value_cache;
+    d.block_tables = block_tables;
+    d.context_lens = context_lens;
+    d.cu_q = cu_q_lens;
+    d.starts = (long long*)workspace;
+    d.ws = (float*)((char*)workspace + split_prefix_bytes(num_segs));
+    d.S = num_segs;
+    d.Hq = num_q_heads;
+    d.Hkv = num_kv_heads;
+    d.G = G;
+    d.D = head_dim;
+    d.NB = num_blocks;
+    d.MB = max_blocks_per_seq;
+    d.BS = block_size;
+    d.chunks = 1;
+    d.part_tokens = 0;
+    d.max_parts = 0;
+    d.scale_log2 = c.scale_log2;
+    hipError_t e = pkv::launch_mixed(d, c, dtype, (hipStream_t)stream);
     if (e != hipSuccess) return hip_fail(e, fn);
     return PKV_OK;
 }

@@ -137,6 +137,7 @@ struct MfmaLoop {
             f32x4 sc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
             for (int ks = 0; ks < KS; ++ks) sc = mma_16x16x32<K>(t.k[ks], st.q[ht][ks], sc);
+            mfma_result_fence();
             float sv[4];
 #pragma unroll
             for (int j = 0; j < 4; ++j) sv[j] = sc[j];
@@ -327,14 +328,18 @@ struct MfmaWideLoop {
 
     __device__ __forceinline__ void block(State& st, Tile& t, int valid, float scale_log2) const {
         float sv[2][4];
+        f32x4 sc[2];
 #pragma unroll
         for (int ht = 0; ht < 2; ++ht) {
-            f32x4 sc = {0.f, 0.f, 0.f, 0.f};
+            sc[ht] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-            for (int ks = 0; ks < KS; ++ks) sc = mma_16x16x32<K>(t.k[ks], st.q[ht][ks], sc);
-#pragma unroll
-            for (int j = 0; j < 4; ++j) sv[ht][j] = sc[j];
+            for (int ks = 0; ks < KS; ++ks) sc[ht] = mma_16x16x32<K>(t.k[ks], st.q[ht][ks], sc[ht]);
         }
+        mfma_result_fence();
+#pragma unroll
+        for (int ht = 0; ht < 2; ++ht)
+#pragma unroll
+            for (int j = 0; j < 4; ++j) sv[ht][j] = sc[ht][j];
         if (valid < kTileTokens) {
 #pragma unroll
             for (int ht = 0; ht < 2; ++ht)

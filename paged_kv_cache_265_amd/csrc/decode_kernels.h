@@ -37,6 +37,23 @@ namespace {
 // 16-token tiles of a context of ctx tokens
 __device__ __forceinline__ int ntiles(int ctx) { return ctx > 0 ? (ctx + kTileTokens - 1) / kTileTokens : 0; }
 
+// Sequence s of a flattened batch is a decode sequence when its segment has one
+// query row; dec_ctx is its context as the decode sees it (0 for other segments,
+// which then hold no units), row_of its query/output row.
+__device__ __forceinline__ bool is_decode(const DecodeParams& p, int s) {
+    return !p.cu_q || p.cu_q[s + 1] - p.cu_q[s] == 1;
+}
+__device__ __forceinline__ int dec_ctx(const DecodeParams& p, int s) { return is_decode(p, s) ? p.context_lens[s] : 0; }
+__device__ __forceinline__ size_t row_of(const DecodeParams& p, int s) { return p.cu_q ? (size_t)p.cu_q[s] : (size_t)s; }
+// the same with a wave-uniform s, through scalar loads
+__device__ __forceinline__ int dec_ctx_uniform(const DecodeParams& p, int s) {
+    if (p.cu_q && scalar_load(p.cu_q, (size_t)s + 1) - scalar_load(p.cu_q, s) != 1) return 0;
+    return scalar_load(p.context_lens, s);
+}
+__device__ __forceinline__ size_t row_of_uniform(const DecodeParams& p, int s) {
+    return p.cu_q ? (size_t)scalar_load(p.cu_q, s) : (size_t)s;
+}
+
 // source of tile b of sequence s for kv head kvh (scalar loads of the block table;
 // s and b are wave-uniform)
 template <int BS>
@@ -93,7 +110,7 @@ __device__ long long total_blocks(const DecodeParams& p, int lane) {
     long long tot = 0;
     for (int base = 0; base < p.S; base += 64) {
         const int s = base + lane;
-        tot += wave_sum_int(s < p.S ? ntiles(p.context_lens[s]) : 0);
+        tot += wave_sum_int(s < p.S ? ntiles(dec_ctx(p, s)) : 0);
     }
     return tot;
 }
@@ -106,12 +123,11 @@ __host__ __device__ __forceinline__ long long wave_of(long long u, long long U, 
 // ---------------------------------------------------------------------------------------
 // balanced split
 // ---------------------------------------------------------------------------------------
+// Wave w of N (wave-uniform) takes units [w U / N, (w+1) U / N).
 template <class Loop, int R>
-__global__ __launch_bounds__(64, Loop::kWaves) void decode_split(DecodeParams p) {
+__device__ __forceinline__ void decode_split_wave(const DecodeParams& p, long long w, long long N) {
     constexpr int HT = Loop::HT;
     const int lane = lane_id();
-    const long long N = gridDim.x;
-    const long long w = blockIdx.x;
     const int NS = p.Hkv * p.chunks;
     // The unit count comes out of lane reductions and the range bounds out of 64-bit
     // divisions, which run on the vector unit: all are asserted wave-uniform, so that
@@ -131,7 +147,7 @@ __global__ __launch_bounds__(64, Loop::kWaves) void decode_split(DecodeParams p)
         long long run = 0;
         for (int base = 0;; base += 64) {
             const int s = base + lane;
-            const int ctx = s < p.S ? p.context_lens[s] : 0;
+            const int ctx = s < p.S ? dec_ctx(p, s) : 0;
             const int nb = ntiles(ctx);
             const int incl = wave_incl_scan(nb, lane);
             const unsigned long long hit = __ballot(run + (long long)NS * incl > lo);
@@ -155,7 +171,7 @@ __global__ __launch_bounds__(64, Loop::kWaves) void decode_split(DecodeParams p)
         x.c = 0;
         do {
             ++x.s;
-            x.ctx = x.s < p.S ? scalar_load(p.context_lens, uniform(x.s)) : kTileTokens;
+            x.ctx = x.s < p.S ? dec_ctx_uniform(p, uniform(x.s)) : kTileTokens;
             x.nb = ntiles(x.ctx);
         } while (x.nb == 0);
     };
@@ -188,7 +204,7 @@ __global__ __launch_bounds__(64, Loop::kWaves) void decode_split(DecodeParams p)
         if (done + 1 == cnt || cc.b + 1 == cc.nb) {
             L.finish(st);
             if (seg_b0 == 0 && cc.b + 1 == cc.nb)
-                L.store_out(st, p.out, cc.s, p.Hq, hd.head0, hd.nh);
+                L.store_out(st, p.out, row_of_uniform(p, uniform(cc.s)), p.Hq, hd.head0, hd.nh);
             else
                 L.store_partial(st, p.ws + ((size_t)w * 2 + (first_seg ? 0 : 1)) * rec, cap, hd.nh);
             first_seg = false;
@@ -203,7 +219,7 @@ __global__ __launch_bounds__(64, Loop::kWaves) void decode_split(DecodeParams p)
         if (done == 0 || cc.b == 0) {
             seg_b0 = cc.b;
             hd = stream_heads<HT>(p, cc.c);
-            L.start(st, p.q, cc.s, p.Hq, hd.head0, hd.nh);
+            L.start(st, p.q, row_of_uniform(p, uniform(cc.s)), p.Hq, hd.head0, hd.nh);
             issue(tn);
             vm_wait_le<Loop::kTileLoads>();
         } else {
@@ -225,8 +241,13 @@ __global__ __launch_bounds__(64, Loop::kWaves) void decode_split(DecodeParams p)
     }
 }
 
+template <class Loop, int R>
+__global__ __launch_bounds__(64, Loop::kWaves) void decode_split(DecodeParams p) {
+    decode_split_wave<Loop, R>(p, blockIdx.x, gridDim.x);
+}
+
 // ---------------------------------------------------------------------------------------
-// fixed partitions
+// fixed partitions (plain batches only: cu_q is NULL)
 // ---------------------------------------------------------------------------------------
 template <class Loop>
 __global__ __launch_bounds__(64, Loop::kWaves) void decode_fixed(DecodeParams p) {
@@ -292,7 +313,9 @@ __global__ __launch_bounds__(256) void decode_merge_stream(DecodeParams p, int s
     const int cap = min(p.G, HT);
     const int D = p.D;
     const size_t rec = (size_t)cap * (D + 2);
+    if (!is_decode(p, s)) return;
     const int ctx = p.context_lens[s];
+    const size_t orow = row_of(p, s);
 
     // pieces: fixed partitions 0 .. count-1, or the split waves w0 .. w1 (waves
     // whose unit range is empty wrote nothing; that happens only when U < N)
@@ -307,7 +330,7 @@ __global__ __launch_bounds__(256) void decode_merge_stream(DecodeParams p, int s
         const int nb = ntiles(ctx);
         if (nb == 0) {  // empty context: zero output
             for (int e = threadIdx.x; e < hd.nh * D; e += blockDim.x)
-                store_elem<K>(p.out, ((size_t)s * p.Hq + hd.head0) * D + e, 0.f);
+                store_elem<K>(p.out, (orow * p.Hq + hd.head0) * D + e, 0.f);
             return;
         }
         U = p.starts[p.S];
@@ -362,7 +385,7 @@ __global__ __launch_bounds__(256) void decode_merge_stream(DecodeParams p, int s
             }
             M = mn;
         }
-        store_elem<K>(p.out, ((size_t)s * p.Hq + hd.head0 + h) * D + d, L > 0.f ? O / L : 0.f);
+        store_elem<K>(p.out, (orow * p.Hq + hd.head0 + h) * D + d, L > 0.f ? O / L : 0.f);
     }
 }
 
@@ -389,8 +412,9 @@ __global__ __launch_bounds__(256) void decode_merge_head(DecodeParams p, int spl
     const int c = idx % NS;
     const int s = idx / NS;
     const Heads hd = stream_heads<HT>(p, c);
-    if (h >= hd.nh) return;
+    if (h >= hd.nh || !is_decode(p, s)) return;
     const int ctx = p.context_lens[s];
+    const size_t orow = row_of(p, s);
     const int D = p.D;
     const size_t rec = (size_t)cap * (D + 2);
     const int tid = threadIdx.x;
@@ -405,7 +429,7 @@ __global__ __launch_bounds__(256) void decode_merge_head(DecodeParams p, int spl
     } else {
         const int nb = ntiles(ctx);
         if (nb == 0) {
-            for (int d = tid; d < D; d += 256) store_elem<K>(p.out, ((size_t)s * p.Hq + hd.head0 + h) * D + d, 0.f);
+            for (int d = tid; d < D; d += 256) store_elem<K>(p.out, (orow * p.Hq + hd.head0 + h) * D + d, 0.f);
             return;
         }
         U = p.starts[p.S];
@@ -468,7 +492,7 @@ __global__ __launch_bounds__(256) void decode_merge_head(DecodeParams p, int spl
         const float s0 = M == kNegInf ? 0.f : fast_exp2(M - mn);
         const float s1 = M1 == kNegInf ? 0.f : fast_exp2(M1 - mn);
         const float Lt = L * s0 + L1 * s1;
-        store_elem<K>(p.out, ((size_t)s * p.Hq + hd.head0 + h) * D + d, Lt > 0.f ? (O * s0 + O1 * s1) / Lt : 0.f);
+        store_elem<K>(p.out, (orow * p.Hq + hd.head0 + h) * D + d, Lt > 0.f ? (O * s0 + O1 * s1) / Lt : 0.f);
     }
 }
 
@@ -540,7 +564,7 @@ __global__ __launch_bounds__(256) void decode_merge_fixed(DecodeParams p) {
 // one-wave workgroups of kernel f that fit on the current device at once, at most
 // per_simd per SIMD (a loop sized for one wave per SIMD keeps that shape even when
 // it happens to need fewer registers) (cached)
-int resident_waves(const void* f, int slot, int per_simd) {
+inline int resident_waves(const void* f, int slot, int per_simd) {
     static std::atomic<int> cache[64][128];
     int dev = 0;
     if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) dev = 0;
@@ -558,7 +582,7 @@ int resident_waves(const void* f, int slot, int per_simd) {
 
 // PKV_SPLIT_DEPTH=2 runs the balanced split with a two-tile ring (one block in
 // flight) instead of the inner loop's own depth; both pipelines stay tested
-bool shallow_split() {
+inline bool shallow_split() {
     const char* e = std::getenv("PKV_SPLIT_DEPTH");
     return e && e[0] == '2' && e[1] == 0;
 }

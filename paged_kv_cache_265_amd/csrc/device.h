@@ -164,6 +164,17 @@ template <int kAux> __device__ __forceinline__ uint2 policy_load8(rsrc_t r, uint
     return make_uint2(x.x, x.y);
 }
 
+// Fence between matrix-core products and the first vector-ALU read of their result:
+// nothing is scheduled across it, and 24 wait states separate the two.  Without it
+// the decode loops, sharing a SIMD with other waves' matrix-core work, gave
+// occasional last-bit differences between runs (the lazy softmax reference then
+// moved), which this padding removes.
+__device__ __forceinline__ void mfma_result_fence() {
+    __builtin_amdgcn_sched_barrier(0);
+    asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7");
+    __builtin_amdgcn_sched_barrier(0);
+}
+
 // ---- misc ------------------------------------------------------------------------------
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }

@@ -22,6 +22,10 @@ struct DecodeParams {
     const void* vc;
     const int32_t* block_tables;
     const int32_t* context_lens;
+    // Flattened batch (NULL: sequence s is query/output row s).  Segment s owns rows
+    // cu_q[s] .. cu_q[s+1]-1; only one-row segments are decode sequences, the others
+    // get no units and no output here.
+    const int32_t* cu_q;
     float* ws;        // partial records: acc[cap][D], m[cap], l[cap] (m in log2 units)
     long long* starts;  // balanced split: first unit of every sequence, then the unit count
     int S, Hq, Hkv, G, D, NB, MB;
@@ -77,6 +81,9 @@ hipError_t launch_decode_bs8(const DecodeParams& p, int kind, int path, hipStrea
 hipError_t launch_decode_bs16(const DecodeParams& p, int kind, int path, hipStream_t stream);
 hipError_t launch_decode_bs32(const DecodeParams& p, int kind, int path, hipStream_t stream);
 hipError_t launch_chunked(const ChunkedParams& p, int kind, hipStream_t stream);
+// one launch for a flattened batch: the one-row segments of cp through the decode
+// split described by dp (dp.cu_q = cp.cu_q_lens), the others as chunked tiles
+hipError_t launch_mixed(const DecodeParams& dp, const ChunkedParams& cp, int kind, hipStream_t stream);
 hipError_t launch_reshape_and_cache(const CacheParams& p, int kind, hipStream_t stream);
 hipError_t launch_copy_blocks(const CopyParams& p, int num_layers, hipStream_t stream);
 hipError_t launch_read_probe(const void* buf, size_t bytes, void* sink, hipStream_t stream);

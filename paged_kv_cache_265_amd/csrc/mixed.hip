@@ -1,0 +1,109 @@
+// mixed.hip -- one launch over a flattened batch of decode sequences and chunked-
+// prefill segments, gfx950.
+//
+// The batch is the pages' mixed step: prefill chunks and decode tokens of many
+// requests flattened into one pass ("现代 LLM 推理引擎剖析", sections 1.4 and 2.1).  A
+// segment with one query row is a decode sequence; the others are prefill chunks.
+// What is computed is exactly paged_attention_chunked's result for every segment;
+// only the schedule differs:
+//  * the first decode_wgs workgroups are decode workgroups: each of their four waves
+//    is one wave of the balanced split over the decode sequences' 16-token tiles
+//    (decode_split_wave), so long decode contexts are cut across many waves;
+//  * the remaining workgroups are the chunked-prefill tiles of the other segments
+//    (chunked_tile); tiles of one-row segments return at once.
+// Decode workgroups come first in the grid, so they start first and stream K/V
+// from HBM while prefill tiles keep the matrix cores busy beside them; when the
+// decode waves are done their slots go to the remaining prefill tiles.  The merge
+// of split decode streams runs as a second, small launch.
+//
+// The whole kernel is sized for two workgroups (two waves per SIMD) per compute
+// unit, the chunked tiles' budget; the decode waves run a three-tile ring.
+#include "chunked_kernels.h"
+#include "decode_kernels.h"
+
+namespace pkv {
+
+namespace {
+
+constexpr int kMixedRing = 3;
+
+template <class Loop, int K, int D, int BS>
+__global__ __launch_bounds__(NW * 64, 2) void mixed_kernel(DecodeParams dp, ChunkedParams cp, int decode_wgs) {
+    __shared__ __attribute__((aligned(16))) char lds[2 * ChunkLds<D>::STAGE];
+    if ((int)blockIdx.x < decode_wgs) {
+        const long long w = (long long)blockIdx.x * NW + uniform((int)(threadIdx.x >> 6));
+        decode_split_wave<Loop, kMixedRing>(dp, w, (long long)decode_wgs * NW);
+    } else {
+        chunked_tile<K, D, BS>(cp, (int)blockIdx.x - decode_wgs, lds, true);
+    }
+}
+
+int compute_units() {
+    static std::atomic<int> cache[64];
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) dev = 0;
+    int v = cache[dev].load(std::memory_order_relaxed);
+    if (v > 0) return v;
+    if (hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || v <= 0) v = 256;
+    cache[dev].store(v, std::memory_order_relaxed);
+    return v;
+}
+
+template <class Loop, int K, int D, int BS>
+hipError_t go(const DecodeParams& dp0, const ChunkedParams& cp, hipStream_t st) {
+    DecodeParams dp = dp0;
+    dp.chunks = (dp.G + Loop::HT - 1) / Loop::HT;
+    const int NS = dp.Hkv * dp.chunks;
+    // one decode workgroup (four waves: one per SIMD) per compute unit
+    int decode_wgs = compute_units();
+    if (decode_wgs * NW > kMaxSplitWaves) decode_wgs = kMaxSplitWaves / NW;
+    const long long tiles = ((long long)cp.max_q_len * cp.G + ROWS_PER_WG - 1) / ROWS_PER_WG;
+    const long long grid = decode_wgs + tiles * cp.Hkv * cp.num_segs;
+    hipLaunchKernelGGL((mixed_kernel<Loop, K, D, BS>), dim3((unsigned)grid), dim3(NW * 64), 0, st, dp, cp,
+                       decode_wgs);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    const int waves = decode_wgs * NW;
+    const int cap = dp.G < Loop::HT ? dp.G : Loop::HT;
+    if (cap <= 8)
+        hipLaunchKernelGGL((decode_merge_stream<K, Loop::HT>), dim3((unsigned)(dp.S * NS)), dim3(256), 0, st, dp,
+                           waves);
+    else
+        hipLaunchKernelGGL((decode_merge_head<K, Loop::HT>), dim3((unsigned)((long long)dp.S * NS * cap)), dim3(256),
+                           0, st, dp, waves);
+    return hipGetLastError();
+}
+
+// decode inner loop as in paged_attention_decode: the vector ALU for one or two
+// query heads per kv head, the matrix cores otherwise
+template <int K, int D, int BS>
+hipError_t pick(const DecodeParams& dp, const ChunkedParams& cp, hipStream_t st) {
+    if (dp.G == 1) return go<ValuLoop<K, D, 1, BS>, K, D, BS>(dp, cp, st);
+    if (dp.G == 2) return go<ValuLoop<K, D, 2, BS>, K, D, BS>(dp, cp, st);
+    if (dp.G <= 16) return go<MfmaLoop<K, D, 1, BS>, K, D, BS>(dp, cp, st);
+    return go<MfmaWideLoop<K, D, BS>, K, D, BS>(dp, cp, st);
+}
+
+template <int K, int D>
+hipError_t by_block_size(const DecodeParams& dp, const ChunkedParams& cp, hipStream_t st) {
+    switch (dp.BS) {
+    case 8: return pick<K, D, 8>(dp, cp, st);
+    case 16: return pick<K, D, 16>(dp, cp, st);
+    case 32: return pick<K, D, 32>(dp, cp, st);
+    default: return hipErrorInvalidValue;
+    }
+}
+
+}  // namespace
+
+hipError_t launch_mixed(const DecodeParams& dp, const ChunkedParams& cp, int kind, hipStream_t st) {
+    switch (kind * 1000 + dp.D) {
+    case KF16 * 1000 + 64: return by_block_size<KF16, 64>(dp, cp, st);
+    case KF16 * 1000 + 128: return by_block_size<KF16, 128>(dp, cp, st);
+    case KBF16 * 1000 + 64: return by_block_size<KBF16, 64>(dp, cp, st);
+    case KBF16 * 1000 + 128: return by_block_size<KBF16, 128>(dp, cp, st);
+    default: return hipErrorInvalidValue;
+    }
+}
+
+}  // namespace pkv

@@ -30,6 +30,8 @@ SYMBOLS = (
     "pkv_decode_workspace_size",
     "paged_attention_decode",
     "paged_attention_chunked",
+    "paged_attention_mixed",
+    "pkv_mixed_workspace_size",
     "reshape_and_cache",
     "copy_blocks",
     "pkv_read_probe",
@@ -66,6 +68,10 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.paged_attention_decode.restype = I
     lib.paged_attention_chunked.argtypes = [P, P, P, I, I, I, P, P, P, P, I, I, I, I, I, I, F, I, P]
     lib.paged_attention_chunked.restype = I
+    lib.paged_attention_mixed.argtypes = [P, P, P, I, I, I, P, P, P, P, I, I, I, I, I, I, F, I, P, Z, P]
+    lib.paged_attention_mixed.restype = I
+    lib.pkv_mixed_workspace_size.argtypes = [I] * 5
+    lib.pkv_mixed_workspace_size.restype = Z
     lib.reshape_and_cache.argtypes = [P, P, P, P, P, I, I, I, I, I, I, P]
     lib.reshape_and_cache.restype = I
     lib.copy_blocks.argtypes = [P, P, I, P, I, I, I, I, I, I, P]
@@ -173,6 +179,35 @@ def paged_attention_chunked(out: torch.Tensor, query: torch.Tensor, cu_q_lens: t
     rc = load_library().paged_attention_chunked(
         _ptr(out), _ptr(query), _ptr(cu_q_lens), cu_q_lens.shape[0] - 1, T, int(max_q_len), _ptr(key_cache),
         _ptr(value_cache), _ptr(block_tables), _ptr(context_lens), Hq, Hkv, D, BS, NB, MB, float(scale), dt,
+        _stream(stream))
+    _check(rc)
+    return out
+
+
+def mixed_workspace_size(num_segs, num_q_heads, num_kv_heads, head_dim, block_size) -> int:
+    return int(load_library().pkv_mixed_workspace_size(num_segs, num_q_heads, num_kv_heads, head_dim, block_size))
+
+
+def paged_attention_mixed(out: torch.Tensor, query: torch.Tensor, cu_q_lens: torch.Tensor, max_q_len: int,
+                          key_cache: torch.Tensor, value_cache: torch.Tensor, block_tables: torch.Tensor,
+                          context_lens: torch.Tensor, scale: float, workspace: Optional[torch.Tensor] = None,
+                          stream=None) -> torch.Tensor:
+    """A flattened batch of decode tokens (one-row segments) and prefill chunks in one
+    attention launch; same arguments and result as paged_attention_chunked (see
+    include/pkv.h).  A workspace is allocated here when none is given."""
+    _contig(out, query, cu_q_lens, key_cache, value_cache, block_tables, context_lens)
+    T, Hq, D = query.shape
+    NB, Hkv, BS, _ = key_cache.shape
+    MB = block_tables.shape[1]
+    S = cu_q_lens.shape[0] - 1
+    dt = _dtype(out, query, key_cache, value_cache)
+    need = mixed_workspace_size(S, Hq, Hkv, D, BS) if S > 0 else 0
+    if workspace is None and need > 0:
+        workspace = torch.empty(need, dtype=torch.uint8, device=query.device)
+    ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    rc = load_library().paged_attention_mixed(
+        _ptr(out), _ptr(query), _ptr(cu_q_lens), S, T, int(max_q_len), _ptr(key_cache), _ptr(value_cache),
+        _ptr(block_tables), _ptr(context_lens), Hq, Hkv, D, BS, NB, MB, float(scale), dt, _ptr(workspace), ws_bytes,
         _stream(stream))
     _check(rc)
     return out

@@ -172,6 +172,41 @@ def test_chunked_empty_is_a_no_op():
     assert _chunked(total_q=0, max_q_len=0, query=None) == 0
 
 
+def _mixed(**over):
+    a = dict(out=FAKE, query=FAKE, cu_q_lens=FAKE, num_segs=2, total_q=10, max_q_len=6, key_cache=FAKE,
+             value_cache=FAKE, block_tables=FAKE, context_lens=FAKE, num_q_heads=8, num_kv_heads=1, head_dim=128,
+             block_size=16, num_blocks=10, max_blocks_per_seq=4, scale=0.1, dtype=2, workspace=FAKE,
+             workspace_bytes=1 << 30, stream=None)
+    a.update(over)
+    return pkv.load_library().paged_attention_mixed(*a.values())
+
+
+@pytest.mark.parametrize("over,code", [
+    ({"dtype": 0}, pkv.pkv.ERR_UNSUPPORTED),
+    ({"block_size": 24}, pkv.pkv.ERR_UNSUPPORTED),
+    ({"head_dim": 80}, pkv.pkv.ERR_UNSUPPORTED),
+    ({"num_segs": -1}, pkv.pkv.ERR_INVALID),
+    ({"max_q_len": 11}, pkv.pkv.ERR_INVALID),
+    ({"cu_q_lens": None}, pkv.pkv.ERR_INVALID),
+    ({"num_q_heads": 7, "num_kv_heads": 2}, pkv.pkv.ERR_INVALID),
+    ({"scale": float("nan")}, pkv.pkv.ERR_INVALID),
+    ({"workspace": None}, pkv.pkv.ERR_WORKSPACE),
+    ({"workspace_bytes": 1000}, pkv.pkv.ERR_WORKSPACE),
+    ({"workspace": FAKE + 8}, pkv.pkv.ERR_INVALID),
+])
+def test_mixed_rejects(over, code):
+    assert _mixed(**over) == code
+    assert pkv.load_library().pkv_last_error()
+
+
+def test_mixed_empty_is_a_no_op_and_workspace_size():
+    assert _mixed(num_segs=0, out=None, workspace=None) == 0
+    assert _mixed(total_q=0, max_q_len=0, query=None) == 0
+    # the balanced-split workspace of the decode call for that many sequences
+    assert pkv.mixed_workspace_size(40, 32, 1, 128, 16) == pkv.decode_workspace_size(40, 32, 1, 128, 16, 1, 0)
+    assert pkv.mixed_workspace_size(0, 32, 1, 128, 16) == 0
+
+
 def _rac(**over):
     a = dict(key=FAKE, value=FAKE, key_cache=FAKE, value_cache=FAKE, slot_mapping=FAKE, num_tokens=3,
              num_kv_heads=8, head_dim=128, block_size=16, num_blocks=10, dtype=2, stream=None)
