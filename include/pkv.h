@@ -101,10 +101,10 @@ int pkv_decode_partition_size(int num_seqs, int num_q_heads, int num_kv_heads, i
 
 /* Bytes of workspace paged_attention_decode needs.
  *   partition_size == 0 (balanced split): a fixed amount that depends on num_seqs,
- *     the heads per kv head and head_dim only -- an int64 per sequence plus room
- *     for two fp32 records of (head_dim + 2) values per query head of a kv head
- *     for each of at most 8192 waves (about 34 MB at 4 query heads per kv head,
- *     head_dim 128).
+ *     the heads per kv head and head_dim only -- an int64 per sequence, then for
+ *     each of at most 8192 waves a 32-byte merge note and room for two fp32
+ *     records of (head_dim + 2) values per query head of a kv head (about 34 MB
+ *     at 4 query heads per kv head, head_dim 128).
  *   partition_size > 0: one such record per (sequence, query head, partition);
  *     zero when every sequence fits one partition (max_blocks_per_seq *
  *     block_size <= partition_size).

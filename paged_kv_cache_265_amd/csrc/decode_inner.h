@@ -45,6 +45,7 @@ struct TileSrc {
 template <int K, int D, int NH, int BS>
 struct MfmaLoop {
     static constexpr int kBS = BS;
+    static constexpr int kElemBytes = Elem<K>::bytes;
     static constexpr int KS = D / 32;
     static constexpr int DT = D / 16;
     static constexpr int HT = 16 * NH;
@@ -244,6 +245,7 @@ struct MfmaLoop {
 template <int K, int D, int BS>
 struct MfmaWideLoop {
     static constexpr int kBS = BS;
+    static constexpr int kElemBytes = Elem<K>::bytes;
     static constexpr int KS = D / 32;
     static constexpr int DQ = D / 32;  // 32-row head_dim tiles of the output
     static constexpr int HT = 32;
@@ -475,6 +477,7 @@ template <int K> __device__ __forceinline__ void widen16(uint4 c, float* f) {
 template <int K, int D, int GT, int BS>
 struct ValuLoop {
     static constexpr int kBS = BS;
+    static constexpr int kElemBytes = Elem<K>::bytes;
     static constexpr int EB = Elem<K>::bytes;
     static constexpr int VE = 16 / EB;                 // elements per 16-byte chunk
     static constexpr int KC = D / VE / 4;              // K chunks per lane

@@ -105,12 +105,32 @@ __device__ __forceinline__ Heads stream_heads(const DecodeParams& p, int c) {
     return h;
 }
 
-// sum over all sequences of their tile counts
-__device__ long long total_blocks(const DecodeParams& p, int lane) {
+// Sum over all sequences of their tile counts, with every context length of a round
+// of 256 sequences loaded at once.  Wave w of N also writes the zero output of each
+// empty decode sequence s with s % N == w (16-byte stores of a whole output row).
+template <int EB>
+__device__ long long total_blocks(const DecodeParams& p, int lane, int w, int N) {
     long long tot = 0;
-    for (int base = 0; base < p.S; base += 64) {
-        const int s = base + lane;
-        tot += wave_sum_int(s < p.S ? ntiles(dec_ctx(p, s)) : 0);
+    for (int base = 0; base < p.S; base += 256) {
+        int nb[4];
+        bool empty[4];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const int s = base + 64 * j + lane;
+            const bool dec = s < p.S && is_decode(p, s);
+            nb[j] = dec ? ntiles(p.context_lens[s]) : 0;
+            empty[j] = dec && nb[j] == 0 && s % N == w;
+        }
+        tot += wave_sum_int(nb[0] + nb[1] + nb[2] + nb[3]);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            for (unsigned long long e = __ballot(empty[j]); e; e &= e - 1) {
+                const int s = base + 64 * j + __builtin_ctzll(e);
+                const size_t n16 = (size_t)p.Hq * p.D * EB / 16;
+                uint4* row = (uint4*)((char*)p.out + row_of_uniform(p, s) * p.Hq * p.D * EB);
+                for (size_t i = lane; i < n16; i += 64) row[i] = make_uint4(0, 0, 0, 0);
+            }
+        }
     }
     return tot;
 }
@@ -132,12 +152,15 @@ __device__ __forceinline__ void decode_split_wave(const DecodeParams& p, long lo
     // The unit count comes out of lane reductions and the range bounds out of 64-bit
     // divisions, which run on the vector unit: all are asserted wave-uniform, so that
     // the counts and cursors derived from them, and the branches on those, are scalar.
-    const long long U = uniform(total_blocks(p, lane) * NS);
+    const long long U = uniform(total_blocks<Loop::kElemBytes>(p, lane, (int)w, (int)N) * NS);
     const long long lo = uniform(w * U / N), hi = uniform((w + 1) * U / N);
     // starts[s] = unit of sequence s's first block (written by the wave that folds
     // it), starts[S] = U: the merge finds every stream's pieces from these
     if (w == 0 && lane == 0) p.starts[p.S] = U;
-    if (lo >= hi) return;
+    if (lo >= hi) {
+        if (lane == 0) p.desc[w] = MergeDesc{0, U, -1, 0, 0, 0};
+        return;
+    }
 
     // locate unit lo: sequence s whose units [NS*cum(s), NS*cum(s+1)) contain it
     struct Cursor {
@@ -163,6 +186,13 @@ __device__ __forceinline__ void decode_split_wave(const DecodeParams& p, long lo
             }
             run += (long long)NS * read_lane(incl, 63);
         }
+    }
+    // merge note: this wave merges the stream it starts in when that stream began in
+    // an earlier wave and ends in this one
+    if (lane == 0) {
+        const long long a = lo - cur.b;
+        const bool own = cur.b > 0 && a + cur.nb <= hi;
+        p.desc[w] = MergeDesc{a, U, own ? cur.s : -1, cur.c, cur.nb, 0};
     }
     auto advance = [&](Cursor& x) {
         if (++x.b < x.nb) return;
@@ -299,55 +329,32 @@ __global__ __launch_bounds__(64, Loop::kWaves) void decode_fixed(DecodeParams p)
 }
 
 // ---------------------------------------------------------------------------------------
-// balanced split, streams of few query heads: one workgroup per stream merges
-// all its heads, o = sum_i 2^(m_i - M) acc_i / sum_i 2^(m_i - M) l_i.  Sequences
-// with an empty context get their zero output here.
+// balanced split, streams of few query heads: workgroup w merges all heads of the
+// stream whose merge note wave w left (see MergeDesc), if any:
+//   o = sum_i 2^(m_i - M) acc_i / sum_i 2^(m_i - M) l_i.
+// Its pieces are the waves w0 .. w whose unit ranges cut the stream (w0's last
+// record, then slot 0 of the others); when U < N each unit sits alone in its wave.
 // ---------------------------------------------------------------------------------------
 template <int K, int HT>
 __global__ __launch_bounds__(256) void decode_merge_stream(DecodeParams p, int split_waves) {
-    const int NS = p.Hkv * p.chunks;
-    const int stream = blockIdx.x;
-    const int s = stream / NS;
-    const int c = stream - s * NS;
-    const Heads hd = stream_heads<HT>(p, c);
+    // the note, through scalar loads (fields: a, U as int64, then s, c, nb)
+    const int32_t* nt = (const int32_t*)(p.desc + blockIdx.x);
+    const int ns = scalar_load(nt, 4);
+    if (ns < 0) return;
+    const long long a = (long long)(((unsigned long long)(uint32_t)scalar_load(nt, 1) << 32) | (uint32_t)scalar_load(nt, 0));
+    const long long U = (long long)(((unsigned long long)(uint32_t)scalar_load(nt, 3) << 32) | (uint32_t)scalar_load(nt, 2));
+    const int nc = scalar_load(nt, 5), nnb = scalar_load(nt, 6);
+    const long long N = split_waves, w1 = blockIdx.x;
+    const Heads hd = stream_heads<HT>(p, nc);
     const int cap = min(p.G, HT);
     const int D = p.D;
     const size_t rec = (size_t)cap * (D + 2);
-    if (!is_decode(p, s)) return;
-    const int ctx = p.context_lens[s];
-    const size_t orow = row_of(p, s);
-
-    // pieces: fixed partitions 0 .. count-1, or the split waves w0 .. w1 (waves
-    // whose unit range is empty wrote nothing; that happens only when U < N)
-    const float* first_rec = nullptr;
-    long long count = 0, w0 = 0, U = 0, a = 0, N = split_waves;
-    if (split_waves == 0) {
-        const int nparts = ctx > 0 ? (ctx + p.part_tokens - 1) / p.part_tokens : 1;
-        if (nparts <= 1) return;
-        first_rec = p.ws + (size_t)(s * NS + c) * p.max_parts * rec;
-        count = nparts;
-    } else {
-        const int nb = ntiles(ctx);
-        if (nb == 0) {  // empty context: zero output
-            for (int e = threadIdx.x; e < hd.nh * D; e += blockDim.x)
-                store_elem<K>(p.out, (orow * p.Hq + hd.head0) * D + e, 0.f);
-            return;
-        }
-        U = p.starts[p.S];
-        a = p.starts[s] + (long long)c * nb;
-        const long long e = a + nb;
-        w0 = wave_of(a, U, N);
-        const long long w1 = wave_of(e - 1, U, N);
-        if (w0 == w1) return;  // written whole by one wave
-        const long long lo0 = w0 * U / N;
-        first_rec = p.ws + ((size_t)w0 * 2 + (lo0 == a ? 0 : 1)) * rec;  // w0's last segment
-        // U >= N: every wave owns at least one unit, pieces are waves w0 .. w1.
-        // U < N: every non-empty wave owns exactly one unit, pieces are the waves of units a .. e-1.
-        count = U >= N ? w1 - w0 + 1 : nb;
-    }
+    const size_t orow = row_of_uniform(p, ns);
+    const long long w0 = wave_of(a, U, N);
+    const float* first_rec = p.ws + ((size_t)w0 * 2 + (w0 * U / N == a ? 0 : 1)) * rec;  // w0's last segment
+    const long long count = U >= N ? w1 - w0 + 1 : nnb;
     // record of piece i
     auto record = [&](long long i) -> const float* {
-        if (split_waves == 0) return first_rec + i * rec;
         if (i == 0) return first_rec;
         const long long w = U >= N ? w0 + i : wave_of(a + i, U, N);
         return p.ws + (size_t)w * 2 * rec;  // slot 0: that wave's first segment
@@ -398,7 +405,6 @@ __global__ __launch_bounds__(256) void decode_merge_stream(DecodeParams p, int s
 // 256 threads = 2 groups x 128 head_dim lanes; group g folds pieces g, g+2, ... in
 // one online pass, kChunk pieces at a time with all their loads in flight, (M, L, O)
 // rescaled by 2^(M_old - M_new); the two groups are joined through LDS at the end.
-// Balanced split only: sequences with an empty context get their zero output here.
 // ---------------------------------------------------------------------------------------
 template <int K, int HT>
 __global__ __launch_bounds__(256) void decode_merge_head(DecodeParams p, int split_waves) {
@@ -428,10 +434,7 @@ __global__ __launch_bounds__(256) void decode_merge_head(DecodeParams p, int spl
         first = p.ws + (size_t)(s * NS + c) * p.max_parts * rec;
     } else {
         const int nb = ntiles(ctx);
-        if (nb == 0) {
-            for (int d = tid; d < D; d += 256) store_elem<K>(p.out, (orow * p.Hq + hd.head0 + h) * D + d, 0.f);
-            return;
-        }
+        if (nb == 0) return;  // empty context: its zero output comes from the split kernel
         U = p.starts[p.S];
         a = p.starts[s] + (long long)c * nb;
         w0 = wave_of(a, U, N);
@@ -615,7 +618,7 @@ hipError_t run(const DecodeParams& p0, bool split, int slot, hipStream_t st) {
     if (!split)
         hipLaunchKernelGGL((decode_merge_fixed<K, Loop::HT>), dim3(per_head), dim3(256), 0, st, p);
     else if (cap <= 8)
-        hipLaunchKernelGGL((decode_merge_stream<K, Loop::HT>), dim3((unsigned)(p.S * NS)), dim3(256), 0, st, p, waves);
+        hipLaunchKernelGGL((decode_merge_stream<K, Loop::HT>), dim3((unsigned)waves), dim3(256), 0, st, p, waves);
     else
         hipLaunchKernelGGL((decode_merge_head<K, Loop::HT>), dim3(per_head), dim3(256), 0, st, p, waves);
     return hipGetLastError();

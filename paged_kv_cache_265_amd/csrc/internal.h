@@ -15,6 +15,18 @@ constexpr int kTileTokens = 16;
 inline bool supported_block_size(int bs) { return bs == 8 || bs == 16 || bs == 32; }
 constexpr float kLog2eHost = 1.4426950408889634f;
 
+// What wave w of the balanced split leaves for the merge: when the stream at the
+// start of its unit range began in an earlier wave and ends inside the range, w
+// holds that stream's last piece and its merge belongs to w: the stream's first
+// unit a, tile count nb, sequence s and stream c, and the batch's unit count U.
+// s < 0: nothing to merge.
+struct MergeDesc {
+    long long a, U;
+    int s, c, nb, pad;
+};
+static_assert(sizeof(MergeDesc) == 32 && offsetof(MergeDesc, s) == 16 && offsetof(MergeDesc, nb) == 24,
+              "the merge reads the note as eight 32-bit words");
+
 struct DecodeParams {
     void* out;
     const void* q;
@@ -28,6 +40,7 @@ struct DecodeParams {
     const int32_t* cu_q;
     float* ws;        // partial records: acc[cap][D], m[cap], l[cap] (m in log2 units)
     long long* starts;  // balanced split: first unit of every sequence, then the unit count
+    MergeDesc* desc;       // balanced split: one per wave (see MergeDesc)
     int S, Hq, Hkv, G, D, NB, MB;
     int BS;           // tokens per KV block: 8, 16 or 32
     int chunks;       // query-head chunks per kv head (set by the launcher)

@@ -52,8 +52,9 @@ def test_status_strings():
 def test_workspace_size_matches_layout():
     rec = lambda cap, D: cap * (D + 2) * 4  # noqa: E731  acc[cap][D] + m[cap] + l[cap], fp32
     # balanced split (partition_size 0): the start unit of every sequence plus the total
-    # (int64, padded to 256 bytes), then two records per wave for at most 8192 waves
-    starts = lambda S: ((S + 1) * 8 + 255) // 256 * 256  # noqa: E731
+    # (int64, padded to 256 bytes), a 32-byte merge note per wave, then two records per
+    # wave, for at most 8192 waves
+    starts = lambda S: ((S + 1) * 8 + 255) // 256 * 256 + 8192 * 32  # noqa: E731
     assert pkv.decode_partition_size(256, 32, 8, 128, 16, 512) == 0
     assert pkv.decode_workspace_size(256, 32, 8, 128, 16, 512) == starts(256) + 8192 * 2 * rec(4, 128)
     assert pkv.decode_workspace_size(32, 32, 1, 128, 16, 8192) == starts(32) + 8192 * 2 * rec(32, 128)
