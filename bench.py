@@ -129,6 +129,38 @@ def cold_calls(torch, pkv, dev, call, n: int = 20):
     return np.array([a.elapsed_time(b) for a, b in evs])
 
 
+def graph_timing(torch, args, step, call, out, nbytes):
+    """The step, and the decode call alone, captured once in a HIP graph and
+    replayed, as a serving loop would launch them: the same kernels with shorter
+    gaps between launches.  The replayed output must match the eager one bit for bit."""
+    eager = out.clone()
+    res = {}
+    for name, fn in (("step", step), ("call", call)):
+        g = torch.cuda.CUDAGraph()
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(side):
+            fn()
+        torch.cuda.current_stream().wait_stream(side)
+        with torch.cuda.graph(g):
+            fn()
+        for _ in range(args.warmup):
+            g.replay()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(args.steps):
+            g.replay()
+        e1.record()
+        torch.cuda.synchronize()
+        ms = e0.elapsed_time(e1) / args.steps
+        res[f"{name}_ms"] = round(ms, 4)
+        res[f"{name}_GBs"] = round(nbytes / (ms * 1e-3) / 1e9, 1)
+        res[f"{name}_bitwise_equal_to_eager"] = bool(torch.equal(out.view(torch.uint8), eager.view(torch.uint8)))
+        del g
+    return res
+
+
 def read_ceiling(torch, pkv, dev, nbytes: int = 4 << 30) -> float:
     """GB/s of pkv_read_probe over a 4 GiB buffer: the decode kernels' load shape
     with nothing else to do, a practical read ceiling of this device."""
@@ -238,26 +270,42 @@ def main():
     if args.paging_study:
         return paging_study(args, torch, pkv, workloads, dev, case, kc, vc, q, bt, cl, new, part, ws)
 
-    def step(ev=None):
+    def call():
+        pkv.paged_attention_decode(out, q, kc, vc, bt, cl, case.scale, partition_size=part, workspace=ws)
+
+    def step():
         if new is not None:
             pkv.reshape_and_cache(new[0], new[1], kc, vc, new[2])
-        if ev is not None:
-            ev[0].record()
-        pkv.paged_attention_decode(out, q, kc, vc, bt, cl, case.scale, partition_size=part, workspace=ws)
-        if ev is not None:
-            ev[1].record()
+        call()
+
+    def timed(fn, n):
+        # n back-to-back launches between one pair of events on the launch stream:
+        # (GPU ms per launch, wall ms per launch)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        e0.record()
+        for _ in range(n):
+            fn()
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / n, (time.perf_counter() - t0) * 1e3 / n
 
     for _ in range(args.warmup):
         step()
-    torch.cuda.synchronize()
+    # the timed region: K whole steps back to back
+    ms_step, wall_ms_step = timed(step, args.steps)
+    # the decode call alone, K calls back to back (the roofline's launch average)
+    dec_ms, _ = timed(call, args.steps)
+    # per-call spread: each call between its own pair of events
     evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
-    t0 = time.perf_counter()
     for i in range(args.steps):
-        step(evs[i])
+        if new is not None:
+            pkv.reshape_and_cache(new[0], new[1], kc, vc, new[2])
+        evs[i][0].record()
+        call()
+        evs[i][1].record()
     torch.cuda.synchronize()
-    t1 = time.perf_counter()
-    ms_step = (t1 - t0) * 1e3 / args.steps
-    dec_ms = float(np.mean([a.elapsed_time(b) for a, b in evs]))
 
     eb = workloads.DTYPES[case.dtype][2]
     nbytes = workloads.algorithmic_decode_bytes(case.context_lens, case.num_q_heads, case.num_kv_heads,
@@ -267,7 +315,8 @@ def main():
     traffic = traffic_from_profiles(args.workload)
     res = {
         "metric": METRIC, "value": round(value, 1), "unit": "GB/s", "n_gpus": 1, "steps": args.steps,
-        "warmup": args.warmup, "ms_per_step": round(ms_step, 4), "higher_is_better": True, "scaling": "weak",
+        "warmup": args.warmup, "ms_per_step": round(ms_step, 4), "wall_ms_per_step": round(wall_ms_step, 4),
+        "higher_is_better": True, "scaling": "weak",
         "vs_baseline": None, "dtype": case.dtype, "data": "synthetic (seeded N(0,1) K/V/q, shuffled block placement)",
         "config": W["config"],
         "pct_of_peak": round(100.0 * value / PEAK_HBM_GBS, 2),
@@ -282,9 +331,9 @@ def main():
     }
     call_ms = np.array([a.elapsed_time(b) for a, b in evs])
     res["call_ms_p10_p50_p90"] = [round(float(np.percentile(call_ms, q)), 4) for q in (10, 50, 90)]
+    res["graph"] = graph_timing(torch, args, step, call, out, nbytes)
     res["warm_median_GBs"] = round(nbytes / (float(np.median(call_ms)) * 1e-3) / 1e9, 1)
-    cold = cold_calls(torch, pkv, dev, lambda: pkv.paged_attention_decode(out, q, kc, vc, bt, cl, case.scale,
-                                                                        partition_size=part, workspace=ws))
+    cold = cold_calls(torch, pkv, dev, call)
     res["cold_call_ms_p10_p50_p90"] = [round(float(np.percentile(cold, q)), 4) for q in (10, 50, 90)]
     res["cold_median_GBs"] = round(nbytes / (float(np.median(cold)) * 1e-3) / 1e9, 1)
     ceiling = read_ceiling(torch, pkv, dev)
@@ -317,28 +366,34 @@ def run_long(args, p, qd, qc, cu, torch, pkv, workloads, dev):
     scale = 1.0 / np.sqrt(128)
     torch.cuda.synchronize()
 
-    def step(ev=None):
-        pkv.reshape_and_cache(nk, nv, kc, vc, sm)
-        if ev is not None:
-            ev[0].record()
+    def dec():
         pkv.paged_attention_decode(out, q, kc, vc, bt[:S], cl[:S], scale, partition_size=0, workspace=ws)
-        if ev is not None:
-            ev[1].record()
+
+    def chk():
         pkv.paged_attention_chunked(outc, qcd, cud, 512, kc, vc, bt[S:], cl[S:], scale)
-        if ev is not None:
-            ev[2].record()
+
+    def step():
+        pkv.reshape_and_cache(nk, nv, kc, vc, sm)
+        dec()
+        chk()
+
+    def timed(fn, n):
+        # n back-to-back launches between one pair of events: (GPU ms, wall ms) per launch
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        e0.record()
+        for _ in range(n):
+            fn()
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / n, (time.perf_counter() - t0) * 1e3 / n
 
     for _ in range(args.warmup):
         step()
-    torch.cuda.synchronize()
-    evs = [tuple(torch.cuda.Event(enable_timing=True) for _ in range(3)) for _ in range(args.steps)]
-    t0 = time.perf_counter()
-    for i in range(args.steps):
-        step(evs[i])
-    torch.cuda.synchronize()
-    ms_step = (time.perf_counter() - t0) * 1e3 / args.steps
-    dec_ms = float(np.mean([a.elapsed_time(b) for a, b, c in evs]))
-    chk_ms = float(np.mean([b.elapsed_time(c) for a, b, c in evs]))
+    ms_step, wall_ms_step = timed(step, args.steps)
+    dec_ms, _ = timed(dec, args.steps)
+    chk_ms, _ = timed(chk, args.steps)
     # the same decode with fixed 512-token partitions instead of the balanced split
     wsf = torch.empty(pkv.decode_workspace_size(S, 32, 1, 128, 16, p.block_tables.shape[1], 512),
                       dtype=torch.uint8, device=dev)
@@ -387,7 +442,8 @@ def run_long(args, p, qd, qc, cu, torch, pkv, workloads, dev):
     nbytes = workloads.algorithmic_decode_bytes(p.context_lens[:S], 32, 1, 128, 2)
     flops = workloads.algorithmic_chunked_flops(p.context_lens[S:], np.diff(cu), 32, 128)
     res = {"metric": METRIC, "value": round(nbytes / (dec_ms * 1e-3) / 1e9, 1), "unit": "GB/s", "n_gpus": 1,
-           "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_step, 4), "higher_is_better": True,
+           "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_step, 4),
+           "wall_ms_per_step": round(wall_ms_step, 4), "higher_is_better": True,
            "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
            "config": {"workload": "long-context mixed batch: MQA 32/1 decode of 32 seqs (context uniform "
                                   "[16384, 131072]) + 8 chunked-prefill segments of 512 rows over 4096 cached "

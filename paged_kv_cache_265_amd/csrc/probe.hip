@@ -1,7 +1,11 @@
 // probe.hip -- streaming read of a device buffer: a measurement utility that
 // gives the practical HBM read ceiling next to the decode kernels (it is not part
 // of the attention path).  Each wave reads 4 KiB tiles w, w + W, ... with the
-// same non-temporal 16-byte loads the decode kernels use, four tiles in flight.
+// same non-temporal 16-byte loads the decode kernels use.  Its shape is the
+// fastest of a sweep on MI355X (1-8 workgroups of 4 waves per compute unit, 1-8
+// tiles in flight per wave, with and without the non-temporal hint): one
+// workgroup per compute unit with two tiles in flight per wave reads ~7.2 TB/s;
+// more bytes in flight read less (four tiles 6.8-6.9, eight 5.0 TB/s).
 #include "device.h"
 #include "internal.h"
 
@@ -9,7 +13,7 @@ namespace pkv {
 
 namespace {
 
-constexpr int kInFlight = 4;
+constexpr int kInFlight = 2;
 
 __global__ __launch_bounds__(256) void read_probe_kernel(const char* p, size_t tiles, unsigned* sink) {
     const int lane = lane_id();
@@ -42,7 +46,7 @@ hipError_t launch_read_probe(const void* buf, size_t bytes, void* sink, hipStrea
     if (hipGetDevice(&dev) != hipSuccess ||
         hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0)
         cus = 256;
-    hipLaunchKernelGGL(read_probe_kernel, dim3((unsigned)cus * 2), dim3(256), 0, st, (const char*)buf, bytes / 4096,
+    hipLaunchKernelGGL(read_probe_kernel, dim3((unsigned)cus), dim3(256), 0, st, (const char*)buf, bytes / 4096,
                        (unsigned*)sink);
     return hipGetLastError();
 }
