@@ -11,7 +11,7 @@ clipped to [16, 8192]).  The metric is the algorithmic KV+Q bytes read per
 second (every logical token's K and V for every kv head once, plus the
 queries), with sequences per second alongside.
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload gqa|opt13b|long]
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload gqa|opt13b|tiny|long|cow|beam]
 """
 
 from __future__ import annotations
@@ -73,6 +73,12 @@ def build_workload(name: str):
                            "num_seqs": c.num_seqs, "num_q_heads": 32, "num_kv_heads": 8, "head_dim": 128,
                            "block_size": 16, "total_context_tokens": int(c.context_lens.sum()),
                            "max_context": int(c.context_lens.max()), "parallelism": "none (one GPU)"}}
+    if name == "tiny":
+        c = workloads.config_decode(1)
+        return {"decode": c, "new": None, "partition_size": 0,
+                "config": {"workload": "tiny paged decode: 4 seqs, contexts {1, 7, 16, 33}, 4 heads MHA, head_dim 64, "
+                                       "fp32, block 16, 32-block pool (launch latency; a parity case)",
+                           "num_seqs": 4, "total_context_tokens": int(c.context_lens.sum())}}
     if name == "opt13b":
         c = workloads.config_decode(2)
         return {"decode": c, "new": None, "partition_size": 0,
@@ -107,10 +113,31 @@ def cpu_baseline(case, budget_s: float = 10.0):
         runs += 1
     nbytes = workloads.algorithmic_decode_bytes(case.context_lens, case.num_q_heads, case.num_kv_heads,
                                                 case.head_dim, workloads.DTYPES[case.dtype][2])
-    return {"value": round(nbytes * runs / spent / 1e9, 2), "unit": "GB/s", "cores": threads, "kind": "oracle",
-            "sample": f"the whole batch ({case.num_seqs} sequences, {int(case.context_lens.sum())} context "
-                      f"tokens) decoded {runs} times by the fp64 C oracle in {spent:.1f} s wall",
-            "seqs_per_s": round(case.num_seqs * runs / spent, 1)}
+    res = {"value": round(nbytes * runs / spent / 1e9, 2), "unit": "GB/s", "cores": threads, "kind": "oracle",
+           "sample": f"the whole batch ({case.num_seqs} sequences, {int(case.context_lens.sum())} context "
+                     f"tokens) decoded {runs} times by the fp64 C oracle in {spent:.1f} s wall",
+           "seqs_per_s": round(case.num_seqs * runs / spent, 1)}
+    # the same on one thread: one pass over the whole batch
+    oracle.set_threads(1)
+    try:
+        t0 = time.perf_counter()
+        oracle.decode(case.query, pool.key_cache, pool.value_cache, case.block_tables, case.context_lens,
+                      case.num_kv_heads, case.block_size, case.scale, case.dtype)
+        one = time.perf_counter() - t0
+    finally:
+        oracle.set_threads(threads)
+    res["single_thread"] = {"value": round(nbytes / one / 1e9, 3), "unit": "GB/s", "cores": 1,
+                            "sample": f"the whole batch decoded once in {one:.1f} s wall",
+                            "seqs_per_s": round(case.num_seqs / one, 1)}
+    cpu = ""
+    try:
+        with open("/proc/cpuinfo") as f:
+            cpu = next((ln.split(":", 1)[1].strip() for ln in f if ln.startswith("model name")), "")
+    except OSError:
+        pass
+    res["cpu_model"] = cpu
+    res["os_cpu_count"] = os.cpu_count()
+    return res
 
 
 def cold_calls(torch, pkv, dev, call, n: int = 20):
@@ -204,7 +231,7 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
-    ap.add_argument("--workload", default="gqa", choices=["gqa", "opt13b", "long", "cow", "beam"])
+    ap.add_argument("--workload", default="gqa", choices=["gqa", "opt13b", "tiny", "long", "cow", "beam"])
     ap.add_argument("--partition-size", type=int, default=None)
     ap.add_argument("--paging-study", action="store_true",
                     help="time the decode call on the same batch with shuffled and with contiguous block "

@@ -46,6 +46,10 @@ def _load():
     lib.oracle_kv_bytes_per_block.argtypes = [I, I, I, I]
     lib.oracle_kv_bytes_per_block.restype = LL
     lib.oracle_decode_element.argtypes = [P, LL, I]
+    lib.oracle_set_threads.argtypes = [I]
+    lib.oracle_set_threads.restype = None
+    lib.oracle_max_threads.argtypes = []
+    lib.oracle_max_threads.restype = I
     lib.oracle_decode_element.restype = D
     for f in (lib.oracle_decode, lib.oracle_chunked, lib.oracle_reshape_and_cache, lib.oracle_copy_blocks):
         f.restype = I
@@ -177,3 +181,12 @@ def decode_elements(raw, dtype: str) -> np.ndarray:
     flat = a.reshape(-1)
     lib = _load()
     return np.array([lib.oracle_decode_element(_p(flat), i, _DT[dtype]) for i in range(flat.size)])
+
+
+def set_threads(n: int) -> None:
+    """Threads of the oracle's parallel loops (timing only; results do not depend on it)."""
+    _load().oracle_set_threads(int(n))
+
+
+def max_threads() -> int:
+    return int(_load().oracle_max_threads())

@@ -37,6 +37,7 @@
  * their bit patterns (fp32, IEEE binary16, bfloat16) by the decoders below.
  */
 #include <math.h>
+#include <omp.h>
 #include <stdint.h>
 #include <stdlib.h>
 #include <string.h>
@@ -289,3 +290,8 @@ long long oracle_kv_bytes_per_block(int block_size, int num_kv_heads, int head_d
 double oracle_decode_element(const void* base, long long index, int dtype) {
     return load(base, (size_t)index, dtype);
 }
+
+/* Threads used by the parallel loops above (timing only: every (sequence, head)
+ * row is computed on its own, so results do not depend on it). */
+void oracle_set_threads(int n) { omp_set_num_threads(n > 0 ? n : 1); }
+int oracle_max_threads(void) { return omp_get_max_threads(); }
