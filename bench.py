@@ -591,32 +591,38 @@ def run_cow(args, torch, pkv, workloads, dev):
                                                c.block_size, c.max_blocks_per_seq, 0), dtype=torch.uint8, device=dev)
     torch.cuda.synchronize()
 
-    def step(ev=None):
+    def dec():
+        pkv.paged_attention_decode(out, q, kc, vc, bt, cl, c.scale, workspace=ws)
+
+    def step():
         pkv.copy_blocks([kc], [vc], bm)
         pkv.reshape_and_cache(nk, nv, kc, vc, sm)
-        if ev is not None:
-            ev[0].record()
-        pkv.paged_attention_decode(out, q, kc, vc, bt, cl, c.scale, workspace=ws)
-        if ev is not None:
-            ev[1].record()
+        dec()
+
+    def timed(fn, n):
+        # n back-to-back launches between one pair of events: (GPU ms, wall ms) per launch
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        e0.record()
+        for _ in range(n):
+            fn()
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / n, (time.perf_counter() - t0) * 1e3 / n
 
     for _ in range(args.warmup):
         step()
-    torch.cuda.synchronize()
-    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
-    t0 = time.perf_counter()
-    for i in range(args.steps):
-        step(evs[i])
-    torch.cuda.synchronize()
-    ms_step = (time.perf_counter() - t0) * 1e3 / args.steps
-    dec_ms = float(np.mean([a.elapsed_time(b) for a, b in evs]))
+    ms_step, wall_ms_step = timed(step, args.steps)
+    dec_ms, _ = timed(dec, args.steps)
     eb = workloads.DTYPES[c.dtype][2]
     logical = workloads.algorithmic_decode_bytes(c.context_lens, c.num_q_heads, c.num_kv_heads, c.head_dim, eb)
     nb = (c.context_lens.astype(np.int64) + c.block_size - 1) // c.block_size
     used = np.unique(np.concatenate([c.block_tables[s, :nb[s]] for s in range(c.num_seqs)]))
     unique = int(len(used)) * c.num_kv_heads * c.block_size * c.head_dim * 2 * eb
     res = {"metric": METRIC, "value": round(logical / (ms_step * 1e-3) / 1e9, 1), "unit": "GB/s", "n_gpus": 1,
-           "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_step, 4), "higher_is_better": True,
+           "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_step, 4),
+           "wall_ms_per_step": round(wall_ms_step, 4), "higher_is_better": True,
            "scaling": "weak", "vs_baseline": None, "dtype": c.dtype, "data": "synthetic",
            "config": {"workload": "prefix sharing: 16 prompts (1024 - U{1..15} tokens) x 8 samples with U{0..256} "
                                   "private tokens, GQA 32/8, head_dim 128, bf16; step = copy_blocks of the "
@@ -626,9 +632,13 @@ def run_cow(args, torch, pkv, workloads, dev):
            "logical_bytes": logical, "unique_bytes": unique,
            "decode_logical_GBs": round(logical / (dec_ms * 1e-3) / 1e9, 1),
            "decode_unique_GBs": round(unique / (dec_ms * 1e-3) / 1e9, 1),
-           "roofline": {"bound": "hbm", "kernel": "paged_attention_decode (unique tiles)",
-                        "achieved": round(unique / (dec_ms * 1e-3) / 1e9, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
-                        "frac": round(unique / (dec_ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4), "traffic": None}}
+           # logical bytes, as for the other workloads: a shared prompt tile counts once per sample that
+           # reads it (the repeats mostly come from the 256 MB last-level cache, so this rate can pass
+           # the HBM peak); decode_unique_GBs counts every distinct tile once
+           "roofline": {"bound": "hbm", "kernel": "paged_attention_decode (logical bytes)",
+                        "achieved": round(logical / (dec_ms * 1e-3) / 1e9, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                        "frac": round(logical / (dec_ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4), "avg_call_ms": round(dec_ms, 4),
+                        "traffic": None}}
     print(json.dumps(res), flush=True)
 
 
