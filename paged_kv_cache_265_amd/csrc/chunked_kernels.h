@@ -17,10 +17,9 @@
 //   S^T = K Q^T        16x16x32 matrix cores, 16 keys x 16 rows per product
 //   O^T += V^T P^T     16x16x32 matrix cores over all 32 keys of the step, P split
 //                      into high and low 16-bit parts so that it keeps fp32 accuracy
-// LDS layouts (rows padded by 16 bytes, so that the 16 lanes reading one 16-byte
-// column hit 16 distinct bank quads):
-//   K: [32 keys][D] as in the pool tile
-//   V: [D][4 groups][8]: group g holds keys 4g..4g+3 of the step's first 16 keys,
+// LDS layouts (rows padded so that the lanes of one read hit distinct banks):
+//   K: [32 keys][D] as in the pool tile, rows padded by 32 bytes
+//   V: [D][4 groups][8], rows padded by 16 bytes: group g holds keys 4g..4g+3 of the step's first 16 keys,
 //      then keys 16+4g..16+4g+3 -- exactly the 8 keys whose probabilities lane group
 //      g holds after the score product, so one 16-byte read is one matrix-core operand.
 #pragma once
@@ -40,7 +39,11 @@ constexpr int KSTEP = 2 * kTileTokens; // keys per step: two 16-key halves
 
 template <int D>
 struct ChunkLds {
-    static constexpr int KROW = D * 2 + 16;      // bytes per key row of K
+    // K rows padded by 32 bytes: the 32 lanes of a 16-byte K read (16 key rows x two
+    // 16-byte columns) then fall on distinct banks; with 16 bytes of padding two of
+    // them shared banks (MI355X counters on the long mixed batch: LDS bank-conflict
+    // cycles 4.5e7 -> 2.7e7)
+    static constexpr int KROW = D * 2 + 32;      // bytes per key row of K
     static constexpr int VROW = 4 * 16 + 16;     // bytes per head_dim row of V
     static constexpr int KBYTES = KSTEP * KROW;
     static constexpr int VBYTES = D * VROW;
