@@ -75,7 +75,7 @@ int max_parts(int max_blocks_per_seq, int block_size, int part) {
 // and one merge note per wave precede the records
 size_t split_starts_bytes(int num_seqs) { return (((size_t)num_seqs + 1) * 8 + 255) / 256 * 256; }
 size_t split_prefix_bytes(int num_seqs) {
-    return split_starts_bytes(num_seqs) + (size_t)pkv::kMaxSplitWaves * sizeof(pkv::MergeDesc);
+    return split_starts_bytes(num_seqs) + (size_t)pkv::kMaxSplitWaves * sizeof(pkv::MergeNote);
 }
 
 // Largest (query-head chunks x record capacity) over the inner loops a decode
@@ -200,11 +200,11 @@ int paged_attention_decode(void* out, const void* query, const void* key_cache, 
     p.cu_q = nullptr;
     if (partition_size == 0) {
         p.starts = (long long*)workspace;
-        p.desc = (pkv::MergeDesc*)((char*)workspace + split_starts_bytes(num_seqs));
+        p.notes = (pkv::MergeNote*)((char*)workspace + split_starts_bytes(num_seqs));
         p.ws = (float*)((char*)workspace + split_prefix_bytes(num_seqs));
     } else {
         p.starts = nullptr;
-        p.desc = nullptr;
+        p.notes = nullptr;
         p.ws = (float*)workspace;
     }
     p.S = num_seqs;
@@ -343,7 +343,7 @@ int paged_attention_mixed(void* out, const void* query, const int32_t* cu_q_lens
     d.context_lens = context_lens;
     d.cu_q = cu_q_lens;
     d.starts = (long long*)workspace;
-    d.desc = (pkv::MergeDesc*)((char*)workspace + split_starts_bytes(num_segs));
+    d.notes = (pkv::MergeNote*)((char*)workspace + split_starts_bytes(num_segs));
     d.ws = (float*)((char*)workspace + split_prefix_bytes(num_segs));
     d.S = num_segs;
     d.Hq = num_q_heads;

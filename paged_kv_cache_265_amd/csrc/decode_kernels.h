@@ -158,7 +158,7 @@ __device__ __forceinline__ void decode_split_wave(const DecodeParams& p, long lo
     // it), starts[S] = U: the merge finds every stream's pieces from these
     if (w == 0 && lane == 0) p.starts[p.S] = U;
     if (lo >= hi) {
-        if (lane == 0) p.desc[w] = MergeDesc{0, U, -1, 0, 0, 0};
+        if (lane == 0) p.notes[w] = MergeNote{0, U, -1, 0, 0, 0};
         return;
     }
 
@@ -192,7 +192,7 @@ __device__ __forceinline__ void decode_split_wave(const DecodeParams& p, long lo
     if (lane == 0) {
         const long long a = lo - cur.b;
         const bool own = cur.b > 0 && a + cur.nb <= hi;
-        p.desc[w] = MergeDesc{a, U, own ? cur.s : -1, cur.c, cur.nb, 0};
+        p.notes[w] = MergeNote{a, U, own ? cur.s : -1, cur.c, cur.nb, 0};
     }
     auto advance = [&](Cursor& x) {
         if (++x.b < x.nb) return;
@@ -330,7 +330,7 @@ __global__ __launch_bounds__(64, Loop::kWaves) void decode_fixed(DecodeParams p)
 
 // ---------------------------------------------------------------------------------------
 // balanced split, streams of few query heads: workgroup w merges all heads of the
-// stream whose merge note wave w left (see MergeDesc), if any:
+// stream whose merge note wave w left (see MergeNote), if any:
 //   o = sum_i 2^(m_i - M) acc_i / sum_i 2^(m_i - M) l_i.
 // Its pieces are the waves w0 .. w whose unit ranges cut the stream (w0's last
 // record, then slot 0 of the others); when U < N each unit sits alone in its wave.
@@ -338,11 +338,10 @@ __global__ __launch_bounds__(64, Loop::kWaves) void decode_fixed(DecodeParams p)
 template <int K, int HT>
 __global__ __launch_bounds__(256) void decode_merge_stream(DecodeParams p, int split_waves) {
     // the note, through scalar loads (fields: a, U as int64, then s, c, nb)
-    const int32_t* nt = (const int32_t*)(p.desc + blockIdx.x);
+    const int32_t* nt = (const int32_t*)(p.notes + blockIdx.x);
     const int ns = scalar_load(nt, 4);
     if (ns < 0) return;
-    const long long a = (long long)(((unsigned long long)(uint32_t)scalar_load(nt, 1) << 32) | (uint32_t)scalar_load(nt, 0));
-    const long long U = (long long)(((unsigned long long)(uint32_t)scalar_load(nt, 3) << 32) | (uint32_t)scalar_load(nt, 2));
+    const long long a = scalar_load64(nt, 0), U = scalar_load64(nt, 2);
     const int nc = scalar_load(nt, 5), nnb = scalar_load(nt, 6);
     const long long N = split_waves, w1 = blockIdx.x;
     const Heads hd = stream_heads<HT>(p, nc);

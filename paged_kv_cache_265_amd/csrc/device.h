@@ -211,6 +211,12 @@ __device__ __forceinline__ int scalar_load(const int32_t* base, size_t i) {
     return ((const __attribute__((address_space(4))) int32_t*)base)[i];
 }
 
+// the same for a 64-bit value stored as two 32-bit words, low word first
+__device__ __forceinline__ long long scalar_load64(const int32_t* base, size_t i) {
+    const uint32_t lo = (uint32_t)scalar_load(base, i), hi = (uint32_t)scalar_load(base, i + 1);
+    return (long long)(((unsigned long long)hi << 32) | lo);
+}
+
 // value of a wave-uniform register from lane `src` (src must be wave-uniform)
 __device__ __forceinline__ int read_lane(int v, int src) { return __builtin_amdgcn_readlane(v, src); }
 __device__ __forceinline__ float read_lane(float v, int src) {

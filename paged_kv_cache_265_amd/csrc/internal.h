@@ -20,11 +20,11 @@ constexpr float kLog2eHost = 1.4426950408889634f;
 // holds that stream's last piece and its merge belongs to w: the stream's first
 // unit a, tile count nb, sequence s and stream c, and the batch's unit count U.
 // s < 0: nothing to merge.
-struct MergeDesc {
+struct MergeNote {
     long long a, U;
     int s, c, nb, pad;
 };
-static_assert(sizeof(MergeDesc) == 32 && offsetof(MergeDesc, s) == 16 && offsetof(MergeDesc, nb) == 24,
+static_assert(sizeof(MergeNote) == 32 && offsetof(MergeNote, s) == 16 && offsetof(MergeNote, nb) == 24,
               "the merge reads the note as eight 32-bit words");
 
 struct DecodeParams {
@@ -40,7 +40,7 @@ struct DecodeParams {
     const int32_t* cu_q;
     float* ws;        // partial records: acc[cap][D], m[cap], l[cap] (m in log2 units)
     long long* starts;  // balanced split: first unit of every sequence, then the unit count
-    MergeDesc* desc;       // balanced split: one per wave (see MergeDesc)
+    MergeNote* notes;      // balanced split: one per wave (see MergeNote)
     int S, Hq, Hkv, G, D, NB, MB;
     int BS;           // tokens per KV block: 8, 16 or 32
     int chunks;       // query-head chunks per kv head (set by the launcher)
