@@ -429,3 +429,17 @@ def test_oracle_reports_bad_block_id():
     with pytest.raises(oracle.OracleError):
         oracle.decode(case.query, case.pool.key_cache, case.pool.value_cache, bt, case.context_lens, 1, 16, 1.0,
                       "f32")
+
+
+def test_thread_count_does_not_change_results():
+    """The oracle's parallel loops give each (sequence, kv head) row to one thread: one
+    thread and all threads return the same bits (the benchmark times both)."""
+    c = make_decode_case([40], "bf16", [1, 17, 100, 333, 64], 8, 2, 128)
+    args = (c.query, c.pool.key_cache, c.pool.value_cache, c.block_tables, c.context_lens, 2, 16, c.scale, "bf16")
+    many = oracle.max_threads()
+    try:
+        oracle.set_threads(1)
+        one = oracle.decode(*args)
+    finally:
+        oracle.set_threads(many)
+    assert np.array_equal(one, oracle.decode(*args))
