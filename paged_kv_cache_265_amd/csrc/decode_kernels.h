@@ -135,10 +135,20 @@ __device__ long long total_blocks(const DecodeParams& p, int lane, int w, int N)
     return tot;
 }
 
-// Streams of few heads are merged one stream per workgroup, except when the batch has
-// fewer than one stream per kStreamsPerWaveForHeadMerge split waves: then streams are cut
-// into many pieces and each query head gets a workgroup of its own.
-constexpr int kStreamsPerWaveForHeadMerge = 4;
+// Which merge joins the pieces of the balanced split, from what the host knows (the
+// streams of the batch against the split waves):
+//  * at least one stream per four waves (many short streams, each cut into a couple of
+//    pieces) and at most 8 heads per stream: one workgroup per owning wave merges every
+//    head of its stream (decode_merge_stream);
+//  * otherwise one workgroup per (stream, head) (decode_merge_head), with 2 groups of
+//    128 lanes, or 8 when a stream averages more than 64 pieces.
+struct MergeChoice {
+    int kind;  // 0: per stream, 1: per head with 2 groups, 2: per head with 8 groups
+};
+inline MergeChoice merge_choice(long long streams, int cap, int waves) {
+    if (cap <= 8 && streams * 4 >= waves) return {0};
+    return {streams * 64 >= waves ? 1 : 2};
+}
 
 // first wave whose unit range contains unit u (ranges [w U / N, (w+1) U / N))
 __host__ __device__ __forceinline__ long long wave_of(long long u, long long U, long long N) {
@@ -401,107 +411,20 @@ __global__ __launch_bounds__(256) void decode_merge_stream(DecodeParams p, int s
 }
 
 // ---------------------------------------------------------------------------------------
-// balanced split, streams cut into many pieces (few streams per wave, as in a long
-// context of one sequence): workgroup (w, h) merges query head h of the stream whose
-// merge note wave w left (see MergeNote), if any:
-//   o = sum_i 2^(m_i - M) acc_i / sum_i 2^(m_i - M) l_i.
-// Its pieces are the waves w0 .. w whose unit ranges cut the stream (w0's last
-// record, then slot 0 of the others); when U < N each unit sits alone in its wave.
-// 256 threads = 2 groups x 128 head_dim lanes; group g folds pieces g, g+2, ... in
-// one online pass, kChunk pieces at a time with all their loads in flight, and the
-// groups are joined through LDS.  With one workgroup per head a stream of a hundred
-// pieces takes four rounds of loads instead of sixteen; with many short streams the
-// extra workgroups cost more than they save, and the per-stream merge above is used.
-// ---------------------------------------------------------------------------------------
-template <int K, int HT>
-__global__ __launch_bounds__(256) void decode_merge_note_head(DecodeParams p, int split_waves) {
-    constexpr int kChunk = 16;  // pieces per group in flight at once
-    __shared__ float other[128 + 2];
-    const int cap = min(p.G, HT);
-    const long long w1 = blockIdx.x / cap;
-    const int h = blockIdx.x - (int)w1 * cap;
-    // the note, through scalar loads (fields: a, U as int64, then s, c, nb)
-    const int32_t* nt = (const int32_t*)(p.notes + w1);
-    const int ns = scalar_load(nt, 4);
-    if (ns < 0) return;
-    const Heads hd = stream_heads<HT>(p, scalar_load(nt, 5));
-    if (h >= hd.nh) return;
-    const long long a = scalar_load64(nt, 0), U = scalar_load64(nt, 2), N = split_waves;
-    const int D = p.D;
-    const size_t rec = (size_t)cap * (D + 2);
-    const size_t orow = row_of_uniform(p, ns);
-    const long long w0 = wave_of(a, U, N);
-    const float* first = p.ws + ((size_t)w0 * 2 + (w0 * U / N == a ? 0 : 1)) * rec;  // w0's last segment
-    const long long count = U >= N ? w1 - w0 + 1 : scalar_load(nt, 6);
-    auto record = [&](long long i) -> const float* {
-        if (i == 0) return first;
-        return p.ws + (size_t)(U >= N ? w0 + i : wave_of(a + i, U, N)) * 2 * rec;  // slot 0: that wave's first segment
-    };
-    const int tid = threadIdx.x;
-    const int g = tid >> 7, d = tid & 127;
-    const int dd = d < D ? d : 0;  // lanes past head_dim read element 0 and store nothing
-    float M = kNegInf, L = 0.f, O = 0.f;
-    for (long long i0 = g; i0 < count; i0 += 2 * kChunk) {
-        float mv[kChunk], lv[kChunk], av[kChunk];
-#pragma unroll
-        for (int j = 0; j < kChunk; ++j) {
-            mv[j] = kNegInf;
-            lv[j] = av[j] = 0.f;
-            const long long i = i0 + 2 * j;
-            if (i < count) {
-                const float* r = record(i);
-                mv[j] = r[cap * D + h];
-                lv[j] = r[cap * D + cap + h];
-                av[j] = r[h * D + dd];
-            }
-        }
-        float mn = M;
-#pragma unroll
-        for (int j = 0; j < kChunk; ++j) mn = fmaxf(mn, mv[j]);
-        const float sc = fast_exp2(M - mn);  // M = -inf on the first chunk: sc = 0 and L = O = 0 anyway
-        L *= sc;
-        O *= sc;
-#pragma unroll
-        for (int j = 0; j < kChunk; ++j) {
-            const float wt = fast_exp2(mv[j] - mn);
-            L += wt * lv[j];
-            O += wt * av[j];
-        }
-        M = mn;
-    }
-    // join group 1 into group 0 (a group without pieces keeps M = -inf, L = O = 0)
-    if (g == 1) {
-        other[d] = O;
-        if (d == 0) {
-            other[128] = M;
-            other[129] = L;
-        }
-    }
-    __syncthreads();
-    if (g == 0 && d < D) {
-        const float M1 = other[128], L1 = other[129], O1 = other[d];
-        const float mn = fmaxf(M, M1);
-        const float s0 = M == kNegInf ? 0.f : fast_exp2(M - mn);
-        const float s1 = M1 == kNegInf ? 0.f : fast_exp2(M1 - mn);
-        const float Lt = L * s0 + L1 * s1;
-        store_elem<K>(p.out, (orow * p.Hq + hd.head0 + h) * D + d, Lt > 0.f ? (O * s0 + O1 * s1) / Lt : 0.f);
-    }
-}
-
-// ---------------------------------------------------------------------------------------
 // merge of the pieces of a stream, one query head per workgroup:
 //   o = sum_i 2^(m_i - M) acc_i / sum_i 2^(m_i - M) l_i.
 // Pieces: the fixed partitions 0 .. nparts-1 of the stream, or, for the balanced
 // split, the waves w0 .. w1 whose unit ranges cut the stream (w0's last record,
 // then slot 0 of the others; when U < N each unit sits alone in its own wave).
-// 256 threads = 2 groups x 128 head_dim lanes; group g folds pieces g, g+2, ... in
-// one online pass, kChunk pieces at a time with all their loads in flight, (M, L, O)
-// rescaled by 2^(M_old - M_new); the two groups are joined through LDS at the end.
+// NG groups x 128 head_dim lanes (NG = 2, or 8 for streams of hundreds of pieces);
+// group g folds pieces g, g+NG, ... in one online pass, kChunk pieces at a time with
+// all their loads in flight, (M, L, O) rescaled by 2^(M_old - M_new); the groups are
+// joined through LDS at the end.
 // ---------------------------------------------------------------------------------------
-template <int K, int HT>
-__global__ __launch_bounds__(256) void decode_merge_head(DecodeParams p, int split_waves) {
+template <int K, int HT, int NG>
+__global__ __launch_bounds__(NG * 128) void decode_merge_head(DecodeParams p, int split_waves) {
     constexpr int kChunk = 16;  // pieces per group in flight at once
-    __shared__ float other[128 + 2];
+    __shared__ float other[NG - 1][128 + 2];
     const int NS = p.Hkv * p.chunks;
     const int cap = min(p.G, HT);
     int idx = blockIdx.x;
@@ -543,13 +466,13 @@ __global__ __launch_bounds__(256) void decode_merge_head(DecodeParams p, int spl
     const int g = tid >> 7, d = tid & 127;
     const int dd = d < D ? d : 0;  // lanes past head_dim read element 0 and store nothing
     float M = kNegInf, L = 0.f, O = 0.f;
-    for (long long i0 = g; i0 < count; i0 += 2 * kChunk) {
+    for (long long i0 = g; i0 < count; i0 += (long long)NG * kChunk) {
         float mv[kChunk], lv[kChunk], av[kChunk];
 #pragma unroll
         for (int j = 0; j < kChunk; ++j) {
             mv[j] = kNegInf;
             lv[j] = av[j] = 0.f;
-            const long long i = i0 + 2 * j;
+            const long long i = i0 + (long long)NG * j;
             if (i < count) {
                 const float* r = record(i);
                 mv[j] = r[cap * D + h];
@@ -571,23 +494,30 @@ __global__ __launch_bounds__(256) void decode_merge_head(DecodeParams p, int spl
         }
         M = mn;
     }
-    // join group 1 into group 0 (every piece has a finite m, so both M are finite
-    // whenever the group had a piece; a group without pieces keeps M = -inf, L = O = 0)
-    if (g == 1) {
-        other[d] = O;
+    // join groups 1 .. NG-1 into group 0 (every piece has a finite m, so a group's M is
+    // finite whenever it had a piece; a group without pieces keeps M = -inf, L = O = 0)
+    if (g > 0) {
+        other[g - 1][d] = O;
         if (d == 0) {
-            other[128] = M;
-            other[129] = L;
+            other[g - 1][128] = M;
+            other[g - 1][129] = L;
         }
     }
     __syncthreads();
     if (g == 0 && d < D) {
-        const float M1 = other[128], L1 = other[129], O1 = other[d];
-        const float mn = fmaxf(M, M1);
+        float mn = M;
+#pragma unroll
+        for (int k = 0; k < NG - 1; ++k) mn = fmaxf(mn, other[k][128]);
         const float s0 = M == kNegInf ? 0.f : fast_exp2(M - mn);
-        const float s1 = M1 == kNegInf ? 0.f : fast_exp2(M1 - mn);
-        const float Lt = L * s0 + L1 * s1;
-        store_elem<K>(p.out, (orow * p.Hq + hd.head0 + h) * D + d, Lt > 0.f ? (O * s0 + O1 * s1) / Lt : 0.f);
+        float Lt = L * s0, Ot = O * s0;
+#pragma unroll
+        for (int k = 0; k < NG - 1; ++k) {
+            const float Mk = other[k][128];
+            const float sk = Mk == kNegInf ? 0.f : fast_exp2(Mk - mn);
+            Lt += other[k][129] * sk;
+            Ot += other[k][d] * sk;
+        }
+        store_elem<K>(p.out, (orow * p.Hq + hd.head0 + h) * D + d, Lt > 0.f ? Ot / Lt : 0.f);
     }
 }
 
@@ -682,6 +612,18 @@ inline bool shallow_split() {
     return e && e[0] == '2' && e[1] == 0;
 }
 
+// merge of the balanced split's pieces (see merge_choice)
+template <int K, int HT>
+void launch_split_merge(const DecodeParams& p, int NS, int cap, int waves, hipStream_t st) {
+    const long long streams = (long long)p.S * NS;
+    const unsigned per_head = (unsigned)(streams * cap);
+    switch (merge_choice(streams, cap, waves).kind) {
+    case 0: hipLaunchKernelGGL((decode_merge_stream<K, HT>), dim3((unsigned)waves), dim3(256), 0, st, p, waves); break;
+    case 1: hipLaunchKernelGGL((decode_merge_head<K, HT, 2>), dim3(per_head), dim3(256), 0, st, p, waves); break;
+    default: hipLaunchKernelGGL((decode_merge_head<K, HT, 8>), dim3(per_head), dim3(1024), 0, st, p, waves); break;
+    }
+}
+
 template <class Loop, int K>
 hipError_t run(const DecodeParams& p0, bool split, int slot, hipStream_t st) {
     DecodeParams p = p0;
@@ -704,18 +646,12 @@ hipError_t run(const DecodeParams& p0, bool split, int slot, hipStream_t st) {
     }
     hipError_t e = hipGetLastError();
     if (e != hipSuccess || (!split && p.max_parts <= 1)) return e;
-    // few heads per stream: a workgroup per stream; many (MQA-like): one per head
     const int cap = p.G < Loop::HT ? p.G : Loop::HT;
     const unsigned per_head = (unsigned)((long long)p.S * NS * cap);
     if (!split)
         hipLaunchKernelGGL((decode_merge_fixed<K, Loop::HT>), dim3(per_head), dim3(256), 0, st, p);
-    else if (cap <= 8 && (long long)p.S * NS * kStreamsPerWaveForHeadMerge < waves)
-        hipLaunchKernelGGL((decode_merge_note_head<K, Loop::HT>), dim3((unsigned)(waves * cap)), dim3(256), 0, st, p,
-                           waves);
-    else if (cap <= 8)
-        hipLaunchKernelGGL((decode_merge_stream<K, Loop::HT>), dim3((unsigned)waves), dim3(256), 0, st, p, waves);
     else
-        hipLaunchKernelGGL((decode_merge_head<K, Loop::HT>), dim3(per_head), dim3(256), 0, st, p, waves);
+        launch_split_merge<K, Loop::HT>(p, NS, cap, waves, st);
     return hipGetLastError();
 }
 

@@ -65,14 +65,7 @@ hipError_t go(const DecodeParams& dp0, const ChunkedParams& cp, hipStream_t st) 
     if (e != hipSuccess) return e;
     const int waves = decode_wgs * NW;
     const int cap = dp.G < Loop::HT ? dp.G : Loop::HT;
-    if (cap <= 8 && (long long)dp.S * NS * kStreamsPerWaveForHeadMerge < waves)
-        hipLaunchKernelGGL((decode_merge_note_head<K, Loop::HT>), dim3((unsigned)(waves * cap)), dim3(256), 0, st, dp,
-                           waves);
-    else if (cap <= 8)
-        hipLaunchKernelGGL((decode_merge_stream<K, Loop::HT>), dim3((unsigned)waves), dim3(256), 0, st, dp, waves);
-    else
-        hipLaunchKernelGGL((decode_merge_head<K, Loop::HT>), dim3((unsigned)((long long)dp.S * NS * cap)), dim3(256),
-                           0, st, dp, waves);
+    launch_split_merge<K, Loop::HT>(dp, NS, cap, waves, st);
     return hipGetLastError();
 }
 
