@@ -138,15 +138,15 @@ __device__ long long total_blocks(const DecodeParams& p, int lane, int w, int N)
 // Which merge joins the pieces of the balanced split, from what the host knows (the
 // streams of the batch against the split waves):
 //  * at least one stream per four waves (many short streams, each cut into a couple of
-//    pieces) and at most 8 heads per stream: one workgroup per owning wave merges every
-//    head of its stream (decode_merge_stream);
+//    pieces): one workgroup per owning wave merges every head of its stream
+//    (decode_merge_stream);
 //  * otherwise one workgroup per (stream, head) (decode_merge_head), with 2 groups of
 //    128 lanes, or 8 when a stream averages more than 64 pieces.
 struct MergeChoice {
     int kind;  // 0: per stream, 1: per head with 2 groups, 2: per head with 8 groups
 };
 inline MergeChoice merge_choice(long long streams, int cap, int waves) {
-    if (cap <= 8 && streams * 4 >= waves) return {0};
+    if (streams * 4 >= waves) return {0};
     return {streams * 64 >= waves ? 1 : 2};
 }
 
@@ -344,8 +344,9 @@ __global__ __launch_bounds__(64, Loop::kWaves) void decode_fixed(DecodeParams p)
 }
 
 // ---------------------------------------------------------------------------------------
-// balanced split, streams of few query heads: workgroup w merges all heads of the
-// stream whose merge note wave w left (see MergeNote), if any:
+// balanced split, many short streams: workgroup w merges all heads of the stream
+// whose merge note wave w left (see MergeNote), if any (four output elements per
+// thread in flight at once):
 //   o = sum_i 2^(m_i - M) acc_i / sum_i 2^(m_i - M) l_i.
 // Its pieces are the waves w0 .. w whose unit ranges cut the stream (w0's last
 // record, then slot 0 of the others); when U < N each unit sits alone in its wave.
@@ -376,6 +377,7 @@ __global__ __launch_bounds__(256) void decode_merge_stream(DecodeParams p, int s
     // one pass over the pieces, eight at a time so that their loads are in flight
     // together: (M, L, O) folded online, rescaled by 2^(M_old - M_new)
     constexpr int CH = 8;
+#pragma unroll 4
     for (int e = threadIdx.x; e < hd.nh * D; e += blockDim.x) {
         const int h = e / D, d = e - h * D;
         float M = kNegInf, L = 0.f, O = 0.f;
