@@ -248,12 +248,13 @@ def test_balanced_split_edges(depth, dtype, G, Hkv, D, ctx, monkeypatch):
 
 
 @pytest.mark.parametrize("dtype,G,Hkv,ctx", [
-    ("bf16", 4, 8, [32768, 5000]),     # few long streams: per-head merge of ~100 pieces each
-    ("f16", 1, 8, [20000]),            # one query head per stream
+    ("bf16", 4, 8, [32768, 5000]),     # few long streams: per-head merge, 2 groups
+    ("f16", 1, 8, [20000]),            # ~128 pieces per stream: per-head merge, 8 groups
     ("bf16", 4, 8, [300] * 300),       # many streams: per-stream merge
+    ("bf16", 32, 1, [300] * 300),      # many MQA streams: per-stream merge of 32 heads
 ])
-def test_long_streams_and_both_stream_merges(dtype, G, Hkv, ctx):
-    """Batches with few long streams are merged per (owning wave, query head), batches
-    with many streams per stream; both against the oracle."""
+def test_long_streams_and_all_split_merges(dtype, G, Hkv, ctx):
+    """Every merge of the balanced split (per stream for many short streams, per head
+    with two or eight groups for few long ones) against the oracle."""
     case = make_decode_case([47, G, len(ctx)], dtype, ctx, G * Hkv, Hkv, 128)
     check_close(run_decode(case), oracle_decode_case(case), dtype, f"long streams {ctx[:2]}")
