@@ -377,8 +377,7 @@ __global__ __launch_bounds__(256) void decode_merge_stream(DecodeParams p, int s
     // one pass over the pieces, eight at a time so that their loads are in flight
     // together: (M, L, O) folded online, rescaled by 2^(M_old - M_new)
     constexpr int CH = 8;
-#pragma unroll 4
-    for (int e = threadIdx.x; e < hd.nh * D; e += blockDim.x) {
+    auto merge_elem = [&](int e) {
         const int h = e / D, d = e - h * D;
         float M = kNegInf, L = 0.f, O = 0.f;
         for (long long i0 = 0; i0 < count; i0 += CH) {
@@ -409,6 +408,13 @@ __global__ __launch_bounds__(256) void decode_merge_stream(DecodeParams p, int s
             M = mn;
         }
         store_elem<K>(p.out, (orow * p.Hq + hd.head0 + h) * D + d, L > 0.f ? O / L : 0.f);
+    };
+    const int n = hd.nh * D;
+    if (n <= 2 * (int)blockDim.x) {  // few heads: at most two elements per thread
+        for (int e = threadIdx.x; e < n; e += blockDim.x) merge_elem(e);
+    } else {                          // many heads: four elements per thread in flight at once
+#pragma unroll 4
+        for (int e = threadIdx.x; e < n; e += blockDim.x) merge_elem(e);
     }
 }
 
