@@ -11,7 +11,7 @@ clipped to [16, 8192]).  The metric is the algorithmic KV+Q bytes read per
 second (every logical token's K and V for every kv head once, plus the
 queries), with sequences per second alongside.
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload gqa|opt13b|tiny|long|cow|beam]
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload gqa|opt13b|tiny|long|cow|beam|shapes]
 """
 
 from __future__ import annotations
@@ -231,7 +231,7 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
-    ap.add_argument("--workload", default="gqa", choices=["gqa", "opt13b", "tiny", "long", "cow", "beam"])
+    ap.add_argument("--workload", default="gqa", choices=["gqa", "opt13b", "tiny", "long", "cow", "beam", "shapes"])
     ap.add_argument("--partition-size", type=int, default=None)
     ap.add_argument("--paging-study", action="store_true",
                     help="time the decode call on the same batch with shuffled and with contiguous block "
@@ -275,6 +275,8 @@ def main():
         return run_cow(args, torch, pkv, workloads, dev)
     if args.workload == "beam":
         return run_beam(args, torch, pkv, workloads, dev)
+    if args.workload == "shapes":
+        return run_shapes(args, torch, pkv, workloads, dev)
     W = build_workload(args.workload)
     case = W["decode"]
     part = W["partition_size"] if args.partition_size is None else args.partition_size
@@ -640,6 +642,56 @@ def run_cow(args, torch, pkv, workloads, dev):
                         "frac": round(logical / (dec_ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4), "avg_call_ms": round(dec_ms, 4),
                         "traffic": None}}
     print(json.dumps(res), flush=True)
+
+
+# (label, dtype, context lengths, query heads, kv heads): batches from one long sequence
+# to many short ones, whose split streams are merged in different ways
+SHAPES = [
+    ("GQA 32/8 bf16, 1 x 131072", "bf16", [131072], 32, 8),
+    ("GQA 32/8 bf16, 2 x 65536", "bf16", [65536] * 2, 32, 8),
+    ("GQA 32/8 bf16, 8 x 16384", "bf16", [16384] * 8, 32, 8),
+    ("GQA 32/8 bf16, 64 x 2048", "bf16", [2048] * 64, 32, 8),
+    ("MQA 32/1 bf16, 1 x 131072", "bf16", [131072], 32, 1),
+    ("MQA 32/1 bf16, 4 x 131072", "bf16", [131072] * 4, 32, 1),
+    ("MQA 32/1 bf16, 256 x 4096", "bf16", [4096] * 256, 32, 1),
+    ("MHA 40 f16, 1 x 65536", "f16", [65536], 40, 40),
+]
+
+
+def run_shapes(args, torch, pkv, workloads, dev):
+    """The decode call on batches of equal-length sequences, from one long context to
+    many short ones (seeded N(0,1) K/V/q, shuffled placement): the best of three
+    rounds of `steps` calls back to back per shape."""
+    from workloads.gen import make_decode_case
+    rows = []
+    for i, (label, dt, ctx, hq, hkv) in enumerate(SHAPES):
+        c = make_decode_case([265, 90, i], dt, ctx, hq, hkv, 128)
+        kc, vc, q = c.pool.key_cache.to(dev), c.pool.value_cache.to(dev), c.query.to(dev)
+        bt, cl = torch.from_numpy(c.block_tables).to(dev), torch.from_numpy(c.context_lens).to(dev)
+        out = torch.empty_like(q)
+        ws = torch.empty(pkv.decode_workspace_size(c.num_seqs, hq, hkv, 128, 16, c.max_blocks_per_seq, 0),
+                         dtype=torch.uint8, device=dev)
+        nbytes = workloads.algorithmic_decode_bytes(c.context_lens, hq, hkv, 128, workloads.DTYPES[dt][2])
+        best = None
+        for _ in range(3):
+            for _ in range(args.warmup):
+                pkv.paged_attention_decode(out, q, kc, vc, bt, cl, c.scale, workspace=ws)
+            torch.cuda.synchronize()
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            for _ in range(args.steps):
+                pkv.paged_attention_decode(out, q, kc, vc, bt, cl, c.scale, workspace=ws)
+            e1.record()
+            torch.cuda.synchronize()
+            ms = e0.elapsed_time(e1) / args.steps
+            best = ms if best is None else min(best, ms)
+        rows.append({"shape": label, "call_us": round(best * 1e3, 1), "bytes": nbytes,
+                     "GBs": round(nbytes / (best * 1e-3) / 1e9, 1)})
+        log(f"{label}: {best * 1e3:.1f} us")
+        del kc, vc, q, out, ws, c
+        torch.cuda.empty_cache()
+    print(json.dumps({"metric": METRIC, "workload": "decode call over batch shapes", "unit": "GB/s",
+                      "steps": args.steps, "warmup": args.warmup, "shapes": rows}), flush=True)
 
 
 def run_beam(args, torch, pkv, workloads, dev):
