@@ -150,6 +150,19 @@ inline MergeChoice merge_choice(long long streams, int cap, int waves) {
     return {streams * 64 >= waves ? 1 : 2};
 }
 
+// Waves of the balanced split that take units: all N launched, unless the batch has
+// fewer than kUnitsPerWave units per wave; then only enough for that many each (at
+// least kMinWorkingWaves), so that a small batch or one long stream is not cut into a
+// thousand pieces for the merge.  Every wave and both merges compute it from U alone,
+// so it does not depend on the block size.
+constexpr long long kUnitsPerWave = 32;
+constexpr long long kMinWorkingWaves = 64;
+__host__ __device__ __forceinline__ long long working_waves(long long U, long long N) {
+    const long long want = (U + kUnitsPerWave - 1) / kUnitsPerWave;
+    const long long n = want > kMinWorkingWaves ? want : kMinWorkingWaves;
+    return n < N ? n : N;
+}
+
 // first wave whose unit range contains unit u (ranges [w U / N, (w+1) U / N))
 __host__ __device__ __forceinline__ long long wave_of(long long u, long long U, long long N) {
     return ((u + 1) * N - 1) / U;
@@ -158,17 +171,19 @@ __host__ __device__ __forceinline__ long long wave_of(long long u, long long U, 
 // ---------------------------------------------------------------------------------------
 // balanced split
 // ---------------------------------------------------------------------------------------
-// Wave w of N (wave-uniform) takes units [w U / N, (w+1) U / N).
+// Wave w of the N launched (wave-uniform) takes units [w U / Nw, (w+1) U / Nw) of the
+// U units, Nw = working_waves(U, N); waves w >= Nw take none.
 template <class Loop, int R>
-__device__ __forceinline__ void decode_split_wave(const DecodeParams& p, long long w, long long N) {
+__device__ __forceinline__ void decode_split_wave(const DecodeParams& p, long long w, long long N_launched) {
     constexpr int HT = Loop::HT;
     const int lane = lane_id();
     const int NS = p.Hkv * p.chunks;
     // The unit count comes out of lane reductions and the range bounds out of 64-bit
     // divisions, which run on the vector unit: all are asserted wave-uniform, so that
     // the counts and cursors derived from them, and the branches on those, are scalar.
-    const long long U = uniform(total_blocks<Loop::kElemBytes>(p, lane, (int)w, (int)N) * NS);
-    const long long lo = uniform(w * U / N), hi = uniform((w + 1) * U / N);
+    const long long U = uniform(total_blocks<Loop::kElemBytes>(p, lane, (int)w, (int)N_launched) * NS);
+    const long long N = uniform(working_waves(U, N_launched));
+    const long long lo = w < N ? uniform(w * U / N) : U, hi = w < N ? uniform((w + 1) * U / N) : U;
     // starts[s] = unit of sequence s's first block (written by the wave that folds
     // it), starts[S] = U: the merge finds every stream's pieces from these
     if (w == 0 && lane == 0) p.starts[p.S] = U;
@@ -357,9 +372,9 @@ __global__ __launch_bounds__(256) void decode_merge_stream(DecodeParams p, int s
     const int32_t* nt = (const int32_t*)(p.notes + blockIdx.x);
     const int ns = scalar_load(nt, 4);
     if (ns < 0) return;
-    const long long a = scalar_load64(nt, 0), U = scalar_load64(nt, 2);
+    const long long a = scalar_load64(nt, 0), U = scalar_load64(nt, 2), N = working_waves(U, split_waves);
     const int nc = scalar_load(nt, 5), nnb = scalar_load(nt, 6);
-    const long long N = split_waves, w1 = blockIdx.x;
+    const long long w1 = blockIdx.x;
     const Heads hd = stream_heads<HT>(p, nc);
     const int cap = min(p.G, HT);
     const int D = p.D;
@@ -449,7 +464,7 @@ __global__ __launch_bounds__(NG * 128) void decode_merge_head(DecodeParams p, in
     const int tid = threadIdx.x;
 
     long long count, w0 = 0, U = 0, a = 0;
-    const long long N = split_waves;
+    long long N = split_waves;
     const float* first;
     if (split_waves == 0) {
         count = ctx > 0 ? (ctx + p.part_tokens - 1) / p.part_tokens : 1;
@@ -459,6 +474,7 @@ __global__ __launch_bounds__(NG * 128) void decode_merge_head(DecodeParams p, in
         const int nb = ntiles(ctx);
         if (nb == 0) return;  // empty context: its zero output comes from the split kernel
         U = p.starts[p.S];
+        N = working_waves(U, split_waves);
         a = p.starts[s] + (long long)c * nb;
         w0 = wave_of(a, U, N);
         const long long w1 = wave_of(a + nb - 1, U, N);
