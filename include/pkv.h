@@ -222,9 +222,10 @@ int copy_blocks(void* const* key_caches, void* const* value_caches, int num_laye
  * pkv_read_probe -- measurement utility, not part of the attention path.
  *
  * Streams `bytes` bytes of device memory at `buf` with the non-temporal 16-byte
- * loads the decode kernels use (each wave reads whole 4 KiB tiles, four in
- * flight), so that a caller can time the practical HBM read ceiling next to a
- * decode call.
+ * loads the decode kernels use (one workgroup of four waves per compute unit,
+ * each wave reading whole 4 KiB tiles, two in flight: the fastest shape of a
+ * sweep on MI355X), so that a caller can time the practical HBM read ceiling
+ * next to a decode call.
  *   buf:   device pointer, 16-byte aligned; bytes: a positive multiple of 4096.
  *   sink:  device buffer of at least 4 bytes; it is written only if the XOR of
  *          all words read equals 0x9e3779b9 (never for a zero-filled buffer), which
