@@ -672,7 +672,9 @@ hipError_t run(const DecodeParams& p0, bool split, int slot, hipStream_t st) {
     if (e != hipSuccess || (!split && p.max_parts <= 1)) return e;
     const int cap = p.G < Loop::HT ? p.G : Loop::HT;
     const unsigned per_head = (unsigned)((long long)p.S * NS * cap);
-    if (!split)
+    if (!split && cap > 8)  // many heads, hundreds of partitions: the online per-head merge
+        hipLaunchKernelGGL((decode_merge_head<K, Loop::HT, 2>), dim3(per_head), dim3(256), 0, st, p, 0);
+    else if (!split)
         hipLaunchKernelGGL((decode_merge_fixed<K, Loop::HT>), dim3(per_head), dim3(256), 0, st, p);
     else
         launch_split_merge<K, Loop::HT>(p, NS, cap, waves, st);
