@@ -2,9 +2,10 @@
 
 1 tiny MHA fp32; 2 OPT-13B-shaped MHA fp16; 3 GQA 32/8 bf16 with the new tokens
 written by reshape_and_cache first; 4 prefix-shared parallel sampling with
-copy-on-write; 5 long-context MQA decode (512-token partitions + reduce) and
-chunked prefill.  Workloads 1-4 are compared in full; workload 5 on sampled
-sequences and sampled query rows that the oracle computes one by one."""
+copy-on-write; 5 long-context MQA decode and chunked prefill.  Every output
+element of every workload is compared; workload 5 under both decode schedules
+(balanced split and 512-token partitions), through the chunked call, and as one
+flattened batch through paged_attention_mixed."""
 
 import numpy as np
 import pytest
@@ -82,54 +83,92 @@ def test_config4_prefix_sharing_copy_on_write():
         np.testing.assert_allclose(ref[s], brute.attention_rows(c.query[s], k, v, c.scale), rtol=1e-10, atol=1e-10)
 
 
+class LongMixed:
+    """Workload 5 on the device, with the oracle's results computed once and shared
+    by the tests below: the 32 MQA decode sequences, and the 8 chunks of 512 rows
+    after their K/V have been written by reshape_and_cache."""
+
+    S, SEGS, L = 32, 8, 512
+    SCALE = 1.0 / np.sqrt(128)
+
+    def __init__(self):
+        p, qd, qc, cu = workloads.config_long_mixed()
+        say(f"workload 5: decode tokens={int(p.context_lens[:self.S].sum())} pool blocks={p.pool.num_blocks}")
+        self.p, self.qd, self.qc, self.cu = p, qd, qc, cu
+        pend = np.nonzero(p.pending)[0]
+        ti = torch.from_numpy(pend)
+        self.nk, self.nv, self.sm = p.logical_k[ti].contiguous(), p.logical_v[ti].contiguous(), p.token_slots[pend]
+        self.kc, self.vc = dev(p.pool.key_cache), dev(p.pool.value_cache)
+        pkv.reshape_and_cache(dev(self.nk), dev(self.nv), self.kc, self.vc, dev(self.sm))
+        torch.cuda.synchronize()
+        self.pool = p.pool.clone()  # host copy after the same write, for the oracle
+        oracle.reshape_and_cache(self.nk, self.nv, self.pool.key_cache, self.pool.value_cache, self.sm, "bf16")
+        self._dec = self._chk = None
+
+    def decode_ref(self):
+        if self._dec is None:
+            say("  oracle: all 32 decode sequences")
+            S = self.S
+            self._dec = oracle.decode(self.qd, self.pool.key_cache, self.pool.value_cache, self.p.block_tables[:S],
+                                      self.p.context_lens[:S], 1, 16, self.SCALE, "bf16")
+        return self._dec
+
+    def chunked_ref(self):
+        if self._chk is None:
+            say("  oracle: all 8 x 512 chunked-prefill rows")
+            S = self.S
+            self._chk = oracle.chunked(self.qc, self.cu, self.pool.key_cache, self.pool.value_cache,
+                                       self.p.block_tables[S:], self.p.context_lens[S:], 1, 16, self.SCALE, "bf16")
+        return self._chk
+
+
 @pytest.fixture(scope="module")
 def long_mixed():
-    p, qd, qc, cu = workloads.config_long_mixed()
-    say(f"workload 5: decode tokens={int(p.context_lens[:32].sum())} pool blocks={p.pool.num_blocks}")
-    return p, qd, qc, cu
+    return LongMixed()
 
 
-def test_config5_long_context_mqa_decode(long_mixed):
-    p, qd, qc, cu = long_mixed
-    S = 32
-    kc, vc = dev(p.pool.key_cache), dev(p.pool.value_cache)
-    bt = dev(p.block_tables[:S])
-    ctx = dev(p.context_lens[:S])
-    q = dev(qd)
-    out = torch.empty_like(q)
-    pkv.paged_attention_decode(out, q, kc, vc, bt, ctx, 1.0 / np.sqrt(128), partition_size=512)
+@pytest.mark.parametrize("partition_size", [0, 512])
+def test_config5_long_context_mqa_decode(long_mixed, partition_size):
+    """Every output element of the 32 long MQA sequences, under the balanced split
+    (partition_size 0, the default) and under fixed 512-token partitions."""
+    w = long_mixed
+    S = w.S
+    say(f"workload 5 decode: partition_size={partition_size}")
+    q = dev(w.qd)
+    out = torch.full_like(q, float("nan"))
+    pkv.paged_attention_decode(out, q, w.kc, w.vc, dev(w.p.block_tables[:S]), dev(w.p.context_lens[:S]), w.SCALE,
+                               partition_size=partition_size)
     torch.cuda.synchronize()
-    sample = [0, 9, int(np.argmax(p.context_lens[:S])), int(np.argmin(p.context_lens[:S]))]
-    ref = oracle.decode(qd[sample], p.pool.key_cache, p.pool.value_cache, p.block_tables[sample],
-                        p.context_lens[sample], 1, 16, 1.0 / np.sqrt(128), "bf16")
-    stats = check_close(out[sample], ref, "bf16", "workload 5 decode")
-    say(f"  sampled seqs {sample}: {stats}")
+    stats = check_close(out, w.decode_ref(), "bf16", f"workload 5 decode, partition_size={partition_size}")
+    say(f"  all {S} sequences: {stats}")
 
 
 def test_config5_chunked_prefill(long_mixed):
-    p, qd, qc, cu = long_mixed
-    S, segs = 32, 8
-    kc, vc = dev(p.pool.key_cache), dev(p.pool.value_cache)
-    pend = np.nonzero(p.pending)[0]
-    ti = torch.from_numpy(pend)
-    nk, nv, sm = p.logical_k[ti].contiguous(), p.logical_v[ti].contiguous(), p.token_slots[pend]
-    pkv.reshape_and_cache(dev(nk), dev(nv), kc, vc, dev(sm))
-    out = torch.empty_like(dev(qc))
-    bt = p.block_tables[S:]
-    ctx = p.context_lens[S:]
-    pkv.paged_attention_chunked(out, dev(qc), dev(cu), 512, kc, vc, dev(bt), dev(ctx), 1.0 / np.sqrt(128))
+    """Every one of the 8 x 512 x 32 chunked-prefill rows."""
+    w = long_mixed
+    S = w.S
+    say("workload 5 chunked prefill: 8 segments x 512 rows")
+    qc = dev(w.qc)
+    out = torch.full_like(qc, float("nan"))
+    pkv.paged_attention_chunked(out, qc, dev(w.cu), w.L, w.kc, w.vc, dev(w.p.block_tables[S:]),
+                                dev(w.p.context_lens[S:]), w.SCALE)
     torch.cuda.synchronize()
-    assert torch.isfinite(out).all()
-    pool = p.pool.clone()
-    oracle.reshape_and_cache(nk, nv, pool.key_cache, pool.value_cache, sm, "bf16")
-    rows, tabs, lens = [], [], []
-    rng = np.random.default_rng(51)
-    for i in range(segs):
-        for r in sorted({0, 1, 255, 511} | set(rng.integers(0, 512, size=4).tolist())):
-            rows.append(int(cu[i]) + r)
-            tabs.append(bt[i])
-            lens.append(int(ctx[i]) - 512 + r + 1)  # row r sees tokens 0 .. n - L + r
-    ref = oracle.decode(qc[rows], pool.key_cache, pool.value_cache, np.stack(tabs), np.asarray(lens, np.int32), 1,
-                        16, 1.0 / np.sqrt(128), "bf16")
-    stats = check_close(out[rows], ref, "bf16", "workload 5 chunked")
-    say(f"  sampled {len(rows)} rows: {stats}")
+    stats = check_close(out, w.chunked_ref(), "bf16", "workload 5 chunked")
+    say(f"  all {out.shape[0]} rows: {stats}")
+
+
+def test_config5_mixed_flattened_batch(long_mixed):
+    """The whole workload as one flattened batch through paged_attention_mixed: the
+    32 decode tokens as one-row segments, then the 8 chunks; every row compared."""
+    w = long_mixed
+    S = w.S
+    cum = np.concatenate([np.arange(S + 1), S + w.cu[1:]]).astype(np.int32)
+    say(f"workload 5 mixed: {len(cum) - 1} segments, {int(cum[-1])} rows")
+    qm = dev(torch.cat([w.qd, w.qc]).contiguous())
+    out = torch.full_like(qm, float("nan"))
+    pkv.paged_attention_mixed(out, qm, dev(cum), w.L, w.kc, w.vc, dev(w.p.block_tables), dev(w.p.context_lens),
+                              w.SCALE)
+    torch.cuda.synchronize()
+    s1 = check_close(out[:S], w.decode_ref(), "bf16", "workload 5 mixed, decode rows")
+    s2 = check_close(out[S:], w.chunked_ref(), "bf16", "workload 5 mixed, prefill rows")
+    say(f"  decode rows: {s1}; prefill rows: {s2}")
