@@ -100,11 +100,15 @@ int pkv_decode_partition_size(int num_seqs, int num_q_heads, int num_kv_heads, i
                               int max_blocks_per_seq, int partition_size);
 
 /* Bytes of workspace paged_attention_decode needs.
- *   partition_size == 0 (balanced split): a fixed amount that depends on num_seqs,
- *     the heads per kv head and head_dim only -- an int64 per sequence, then for
- *     each of at most 8192 waves a 32-byte merge note and room for two fp32
- *     records of (head_dim + 2) values per query head of a kv head (about 34 MB
- *     at 4 query heads per kv head, head_dim 128).
+ *   partition_size == 0 (balanced split): depends on num_seqs, the heads per kv
+ *     head, head_dim and the compute units of the current device -- an int64 per
+ *     sequence, then for each wave the split may launch on that device (4 per
+ *     compute unit when its inner loop is built for one wave per SIMD, which is
+ *     the case at head_dim 128 with two or more query heads per kv head; up to 16
+ *     otherwise; at most 8192) a 32-byte merge note and room for two fp32 records of
+ *     (head_dim + 2) values per query head of a kv head: 4.3 MB at 4 query heads
+ *     per kv head and 34 MB at 32, head_dim 128, on MI355X's 256 compute units.
+ *     Size it with the device that will run the call current.
  *   partition_size > 0: one such record per (sequence, query head, partition);
  *     zero when every sequence fits one partition (max_blocks_per_seq *
  *     block_size <= partition_size).

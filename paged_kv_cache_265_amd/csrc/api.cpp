@@ -6,6 +6,7 @@
 
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
@@ -71,11 +72,27 @@ int max_parts(int max_blocks_per_seq, int block_size, int part) {
     return (int)((tokens + part - 1) / part);
 }
 
-// balanced split: the per-sequence start units (S + 1 int64, padded to 256 bytes)
-// and one merge note per wave precede the records
+// Balanced split workspace: the per-sequence start units (S + 1 int64, padded to 256
+// bytes), one merge note per wave the split may launch, then two records per wave.
 size_t split_starts_bytes(int num_seqs) { return (((size_t)num_seqs + 1) * 8 + 255) / 256 * 256; }
-size_t split_prefix_bytes(int num_seqs) {
-    return split_starts_bytes(num_seqs) + (size_t)pkv::kMaxSplitWaves * sizeof(pkv::MergeNote);
+size_t split_prefix_bytes(int num_seqs, long long waves) {
+    return split_starts_bytes(num_seqs) + ((size_t)waves * sizeof(pkv::MergeNote) + 255) / 256 * 256;
+}
+
+// Waves the balanced split launches at most on the current device: every compute
+// unit holds at most kSimdsPerCu x (waves per SIMD of the inner loop); kind < 0
+// takes the largest over the three element types.
+long long split_wave_bound(int kind, int G, int D, int path) {
+    int per_simd = 0;
+    for (int k = PKV_F32; k <= PKV_BF16; ++k)
+        if (kind < 0 || kind == k) per_simd = std::max(per_simd, pkv::split_waves_per_simd(k, G, D, path));
+    const long long w = (long long)pkv::device_compute_units() * pkv::kSimdsPerCu * per_simd;
+    return std::min<long long>(w, pkv::kMaxSplitWaves);
+}
+
+// waves of the single mixed launch's decode part: one four-wave workgroup per compute unit
+long long mixed_decode_waves() {
+    return std::min<long long>((long long)pkv::device_compute_units() * pkv::kSimdsPerCu, pkv::kMaxSplitWaves);
 }
 
 // Largest (query-head chunks x record capacity) over the inner loops a decode
@@ -102,6 +119,28 @@ int decode_path() {
     if (!std::strcmp(e, "valu")) return 1;
     if (!std::strcmp(e, "mfma")) return 2;
     return -1;
+}
+
+// Workspace bytes of a decode (see pkv_decode_workspace_size); kind < 0: enough for
+// every element type.  *waves: the wave bound the balanced split's layout uses.
+size_t decode_need(int num_seqs, int num_q_heads, int num_kv_heads, int head_dim, int block_size,
+                   int max_blocks_per_seq, int partition_size, int kind, int path, long long* waves) {
+    *waves = 0;
+    if (num_seqs <= 0 || num_q_heads <= 0 || num_kv_heads <= 0 || num_q_heads % num_kv_heads != 0 ||
+        head_dim <= 0 || block_size <= 0 || max_blocks_per_seq <= 0 || !partition_ok(partition_size, block_size))
+        return 0;
+    const int G = num_q_heads / num_kv_heads;
+    long long heads_per_kv = 0;
+    int cap = 0;
+    record_shape(G, &heads_per_kv, &cap);
+    const size_t per_head = ((size_t)head_dim + 2) * sizeof(float);
+    if (partition_size == 0) {
+        *waves = split_wave_bound(kind, G, head_dim, path);
+        return split_prefix_bytes(num_seqs, *waves) + (size_t)*waves * 2 * cap * per_head;
+    }
+    const int mp = max_parts(max_blocks_per_seq, block_size, partition_size);
+    if (mp <= 1) return 0;
+    return (size_t)num_seqs * num_kv_heads * heads_per_kv * mp * per_head;
 }
 
 }  // namespace
@@ -138,26 +177,20 @@ int pkv_decode_partition_size(int num_seqs, int num_q_heads, int num_kv_heads, i
 
 size_t pkv_decode_workspace_size(int num_seqs, int num_q_heads, int num_kv_heads, int head_dim, int block_size,
                                  int max_blocks_per_seq, int partition_size) {
-    if (num_seqs <= 0 || num_q_heads <= 0 || num_kv_heads <= 0 || num_q_heads % num_kv_heads != 0 ||
-        head_dim <= 0 || block_size <= 0 || max_blocks_per_seq <= 0 || !partition_ok(partition_size, block_size))
-        return 0;
-    const int G = num_q_heads / num_kv_heads;
-    long long heads_per_kv = 0;
-    int cap = 0;
-    record_shape(G, &heads_per_kv, &cap);
-    const size_t per_head = ((size_t)head_dim + 2) * sizeof(float);
-    if (partition_size == 0) return split_prefix_bytes(num_seqs) + (size_t)pkv::kMaxSplitWaves * 2 * cap * per_head;
-    const int mp = max_parts(max_blocks_per_seq, block_size, partition_size);
-    if (mp <= 1) return 0;
-    return (size_t)num_seqs * num_kv_heads * heads_per_kv * mp * per_head;
+    long long waves = 0;
+    return decode_need(num_seqs, num_q_heads, num_kv_heads, head_dim, block_size, max_blocks_per_seq, partition_size,
+                       -1, 0, &waves);
 }
 
-int paged_attention_decode(void* out, const void* query, const void* key_cache, const void* value_cache,
-                           const int32_t* block_tables, const int32_t* context_lens, int num_seqs,
-                           int num_q_heads, int num_kv_heads, int head_dim, int block_size, int num_blocks,
-                           int max_blocks_per_seq, float scale, int dtype, int partition_size, void* workspace,
-                           size_t workspace_bytes, void* stream) {
-    static const char* fn = "paged_attention_decode";
+}  // extern "C"
+
+namespace {
+
+// paged_attention_decode: validation, workspace check, launch
+int decode_call(const char* fn, void* out, const void* query, const void* key_cache, const void* value_cache,
+                const int32_t* block_tables, const int32_t* context_lens, int num_seqs, int num_q_heads,
+                int num_kv_heads, int head_dim, int block_size, int num_blocks, int max_blocks_per_seq, float scale,
+                int dtype, int partition_size, void* workspace, size_t workspace_bytes, void* stream) {
     int rc;
     if ((rc = check_pool(fn, num_kv_heads, head_dim, block_size, num_blocks, dtype)) != PKV_OK) return rc;
     if ((rc = check_heads(fn, num_q_heads, num_kv_heads)) != PKV_OK) return rc;
@@ -183,12 +216,14 @@ int paged_attention_decode(void* out, const void* query, const void* key_cache, 
     const int G = num_q_heads / num_kv_heads;
     const long long grid = (long long)(mp > 0 ? mp : 1) * num_q_heads * num_seqs;  // bound on workgroups
     if (grid > 0x7fffffffLL) return set_error(PKV_ERR_INVALID, "%s: problem too large for one launch", fn);
-    const size_t need = pkv_decode_workspace_size(num_seqs, num_q_heads, num_kv_heads, head_dim, block_size,
-                                                  max_blocks_per_seq, partition_size);
+    long long waves = 0;
+    const size_t need = decode_need(num_seqs, num_q_heads, num_kv_heads, head_dim, block_size, max_blocks_per_seq,
+                                    partition_size, dtype, path, &waves);
     if (need > 0 && (!workspace || workspace_bytes < need))
         return set_error(PKV_ERR_WORKSPACE, "%s: workspace of %zu bytes needed, %zu given", fn, need,
-                    workspace ? workspace_bytes : (size_t)0);
-    if (need > 0 && !aligned(workspace, 16)) return set_error(PKV_ERR_INVALID, "%s: workspace must be 16-byte aligned", fn);
+                         workspace ? workspace_bytes : (size_t)0);
+    if (need > 0 && !aligned(workspace, 16))
+        return set_error(PKV_ERR_INVALID, "%s: workspace must be 16-byte aligned", fn);
 
     pkv::DecodeParams p;
     p.out = out;
@@ -201,7 +236,7 @@ int paged_attention_decode(void* out, const void* query, const void* key_cache, 
     if (partition_size == 0) {
         p.starts = (long long*)workspace;
         p.notes = (pkv::MergeNote*)((char*)workspace + split_starts_bytes(num_seqs));
-        p.ws = (float*)((char*)workspace + split_prefix_bytes(num_seqs));
+        p.ws = (float*)((char*)workspace + split_prefix_bytes(num_seqs, waves));
     } else {
         p.starts = nullptr;
         p.notes = nullptr;
@@ -222,6 +257,20 @@ int paged_attention_decode(void* out, const void* query, const void* key_cache, 
     hipError_t e = pkv::launch_decode_path(p, dtype, path, (hipStream_t)stream);
     if (e != hipSuccess) return hip_fail(e, fn);
     return PKV_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int paged_attention_decode(void* out, const void* query, const void* key_cache, const void* value_cache,
+                           const int32_t* block_tables, const int32_t* context_lens, int num_seqs,
+                           int num_q_heads, int num_kv_heads, int head_dim, int block_size, int num_blocks,
+                           int max_blocks_per_seq, float scale, int dtype, int partition_size, void* workspace,
+                           size_t workspace_bytes, void* stream) {
+    return decode_call("paged_attention_decode", out, query, key_cache, value_cache, block_tables, context_lens,
+                       num_seqs, num_q_heads, num_kv_heads, head_dim, block_size, num_blocks, max_blocks_per_seq,
+                       scale, dtype, partition_size, workspace, workspace_bytes, stream);
 }
 
 int paged_attention_chunked(void* out, const void* query, const int32_t* cu_q_lens, int num_segs, int total_q,
@@ -276,8 +325,14 @@ int paged_attention_chunked(void* out, const void* query, const int32_t* cu_q_le
 }
 
 size_t pkv_mixed_workspace_size(int num_segs, int num_q_heads, int num_kv_heads, int head_dim, int block_size) {
-    if (num_segs <= 0) return 0;
-    return pkv_decode_workspace_size(num_segs, num_q_heads, num_kv_heads, head_dim, block_size, 1, 0);
+    if (num_segs <= 0 || num_q_heads <= 0 || num_kv_heads <= 0 || num_q_heads % num_kv_heads != 0 ||
+        head_dim <= 0 || block_size <= 0)
+        return 0;
+    long long heads_per_kv = 0;
+    int cap = 0;
+    record_shape(num_q_heads / num_kv_heads, &heads_per_kv, &cap);
+    const long long waves = mixed_decode_waves();
+    return split_prefix_bytes(num_segs, waves) + (size_t)waves * 2 * cap * ((size_t)head_dim + 2) * sizeof(float);
 }
 
 int paged_attention_mixed(void* out, const void* query, const int32_t* cu_q_lens, int num_segs, int total_q,
@@ -344,7 +399,7 @@ int paged_attention_mixed(void* out, const void* query, const int32_t* cu_q_lens
     d.cu_q = cu_q_lens;
     d.starts = (long long*)workspace;
     d.notes = (pkv::MergeNote*)((char*)workspace + split_starts_bytes(num_segs));
-    d.ws = (float*)((char*)workspace + split_prefix_bytes(num_segs));
+    d.ws = (float*)((char*)workspace + split_prefix_bytes(num_segs, mixed_decode_waves()));
     d.S = num_segs;
     d.Hq = num_q_heads;
     d.Hkv = num_kv_heads;

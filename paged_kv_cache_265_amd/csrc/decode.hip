@@ -22,4 +22,28 @@ hipError_t launch_decode(const DecodeParams& p, int kind, hipStream_t st) {
     return launch_decode_path(p, kind, 0, st);
 }
 
+int device_compute_units() {
+    static std::atomic<int> cache[64];
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+    int v = cache[dev].load(std::memory_order_relaxed);
+    if (v > 0) return v;
+    if (hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || v <= 0) v = 256;
+    cache[dev].store(v, std::memory_order_relaxed);
+    return v;
+}
+
+int split_waves_per_simd(int kind, int G, int D, int path) {
+    const bool mfma = kind != KF32 && (path == 2 || (path == 0 && G >= 4));
+    switch (kind * 1000 + D) {
+    case KF32 * 1000 + 64: return per_simd_of<KF32, 64>(G, false);
+    case KF32 * 1000 + 128: return per_simd_of<KF32, 128>(G, false);
+    case KF16 * 1000 + 64: return per_simd_of<KF16, 64>(G, mfma);
+    case KF16 * 1000 + 128: return per_simd_of<KF16, 128>(G, mfma);
+    case KBF16 * 1000 + 64: return per_simd_of<KBF16, 64>(G, mfma);
+    case KBF16 * 1000 + 128: return per_simd_of<KBF16, 128>(G, mfma);
+    default: return 4;
+    }
+}
+
 }  // namespace pkv

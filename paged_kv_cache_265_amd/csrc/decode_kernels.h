@@ -619,15 +619,18 @@ inline int resident_waves(const void* f, int slot, int per_simd) {
     if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) dev = 0;
     int v = cache[dev][slot].load(std::memory_order_relaxed);
     if (v > 0) return v;
-    int cus = 0, per_cu = 0;
-    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0) cus = 256;
+    const int cus = device_compute_units();
+    int per_cu = 0;
     if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, f, 64, 0) != hipSuccess || per_cu <= 0) per_cu = 4;
-    if (per_cu > 4 * per_simd) per_cu = 4 * per_simd;
+    if (per_cu > kSimdsPerCu * per_simd) per_cu = kSimdsPerCu * per_simd;
     v = cus * per_cu;
     if (v > kMaxSplitWaves) v = kMaxSplitWaves;
     cache[dev][slot].store(v, std::memory_order_relaxed);
     return v;
 }
+
+// the waves per SIMD the balanced split allows a loop (see run below)
+template <class Loop> constexpr int split_per_simd() { return Loop::kWaves == 1 ? 1 : 4; }
 
 // PKV_SPLIT_DEPTH=2 runs the balanced split with a two-tile ring (one block in
 // flight) instead of the inner loop's own depth; both pipelines stay tested
@@ -658,7 +661,7 @@ hipError_t run(const DecodeParams& p0, bool split, int slot, hipStream_t st) {
         if (!shallow_split()) {
             // deep-ring loops are built for one wave per SIMD; the others take what fits
             waves = resident_waves((const void*)decode_split<Loop, Loop::kRing>, slot * 2 + 1,
-                                   Loop::kWaves == 1 ? 1 : 4);
+                                   split_per_simd<Loop>());
             hipLaunchKernelGGL((decode_split<Loop, Loop::kRing>), dim3(waves), dim3(64), 0, st, p);
         } else {
             waves = resident_waves((const void*)decode_split<Loop, 2>, slot * 2, 4);
@@ -693,6 +696,19 @@ hipError_t dispatch(const DecodeParams& p, bool mfma, bool split, hipStream_t st
     if (p.G == 1) return run<ValuLoop<K, D, 1, BS>, K>(p, split, base + 2, st);
     if (p.G == 2) return run<ValuLoop<K, D, 2, BS>, K>(p, split, base + 3, st);
     return run<ValuLoop<K, D, 4, BS>, K>(p, split, base + 4, st);
+}
+
+// waves per SIMD of the balanced split for the loop dispatch() picks (block size
+// does not change it)
+template <int K, int D>
+int per_simd_of(int G, bool mfma) {
+    if (shallow_split()) return 4;
+    if constexpr (K != KF32) {
+        if (mfma) return G <= 16 ? split_per_simd<MfmaLoop<K, D, 1, 16>>() : split_per_simd<MfmaWideLoop<K, D, 16>>();
+    }
+    if (G == 1) return split_per_simd<ValuLoop<K, D, 1, 16>>();
+    if (G == 2) return split_per_simd<ValuLoop<K, D, 2, 16>>();
+    return split_per_simd<ValuLoop<K, D, 4, 16>>();
 }
 
 // path: 0 automatic, 1 vector ALU inner loop, 2 matrix-core inner loop (16-bit types)

@@ -49,8 +49,17 @@ struct DecodeParams {
     float scale_log2; // scale * log2(e): scores are kept in log2 units
 };
 
-// upper bound on the one-wave workgroups of the balanced split (sizes its workspace)
+// Upper bound on the one-wave workgroups of the balanced split.  A launch puts at
+// most kSimdsPerCu x (waves per SIMD of its inner loop) of them on each compute
+// unit (split_waves_per_simd), and the workspace is sized for that many.
 constexpr int kMaxSplitWaves = 8192;
+constexpr int kSimdsPerCu = 4;
+// compute units of the current device (cached per device; 256 when unknown)
+int device_compute_units();
+// waves per SIMD that the balanced split of paged_attention_decode launches at most
+// for this element kind, heads per kv head, head_dim and inner-loop choice (path:
+// 0 automatic, 1 vector ALU, 2 matrix cores)
+int split_waves_per_simd(int kind, int G, int D, int path);
 
 struct ChunkedParams {
     void* out;

@@ -38,24 +38,13 @@ __global__ __launch_bounds__(NW * 64, 2) void mixed_kernel(DecodeParams dp, Chun
     }
 }
 
-int compute_units() {
-    static std::atomic<int> cache[64];
-    int dev = 0;
-    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) dev = 0;
-    int v = cache[dev].load(std::memory_order_relaxed);
-    if (v > 0) return v;
-    if (hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || v <= 0) v = 256;
-    cache[dev].store(v, std::memory_order_relaxed);
-    return v;
-}
-
 template <class Loop, int K, int D, int BS>
 hipError_t go(const DecodeParams& dp0, const ChunkedParams& cp, hipStream_t st) {
     DecodeParams dp = dp0;
     dp.chunks = (dp.G + Loop::HT - 1) / Loop::HT;
     const int NS = dp.Hkv * dp.chunks;
     // one decode workgroup (four waves: one per SIMD) per compute unit
-    int decode_wgs = compute_units();
+    int decode_wgs = device_compute_units();
     if (decode_wgs * NW > kMaxSplitWaves) decode_wgs = kMaxSplitWaves / NW;
     const long long tiles = ((long long)cp.max_q_len * cp.G + ROWS_PER_WG - 1) / ROWS_PER_WG;
     const long long grid = decode_wgs + tiles * cp.Hkv * cp.num_segs;

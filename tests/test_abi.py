@@ -52,13 +52,23 @@ def test_status_strings():
 def test_workspace_size_matches_layout():
     rec = lambda cap, D: cap * (D + 2) * 4  # noqa: E731  acc[cap][D] + m[cap] + l[cap], fp32
     # balanced split (partition_size 0): the start unit of every sequence plus the total
-    # (int64, padded to 256 bytes), a 32-byte merge note per wave, then two records per
-    # wave, for at most 8192 waves
-    starts = lambda S: ((S + 1) * 8 + 255) // 256 * 256 + 8192 * 32  # noqa: E731
+    # (int64, padded to 256 bytes), a 32-byte merge note per wave (padded to 256 bytes),
+    # then two records per wave, for as many waves as the split may launch: 4 SIMDs per
+    # compute unit (256 on MI355X, and when no device answers) times the waves per
+    # SIMD of the inner loop -- one for the loops built for one wave per SIMD (head_dim
+    # 128 with two or more query heads per kv head, the 16-head matrix-core loop at 128),
+    # up to four for the others -- the largest over the three element types
+    waves = lambda per_simd: 256 * 4 * per_simd  # noqa: E731
+    starts = lambda S, w: ((S + 1) * 8 + 255) // 256 * 256 + (w * 32 + 255) // 256 * 256  # noqa: E731
     assert pkv.decode_partition_size(256, 32, 8, 128, 16, 512) == 0
-    assert pkv.decode_workspace_size(256, 32, 8, 128, 16, 512) == starts(256) + 8192 * 2 * rec(4, 128)
-    assert pkv.decode_workspace_size(32, 32, 1, 128, 16, 8192) == starts(32) + 8192 * 2 * rec(32, 128)
-    assert pkv.decode_workspace_size(4, 4, 4, 64, 16, 3) == starts(4) + 8192 * 2 * rec(1, 64)
+    w = waves(1)
+    assert pkv.decode_workspace_size(256, 32, 8, 128, 16, 512) == starts(256, w) + w * 2 * rec(4, 128)
+    assert pkv.decode_workspace_size(32, 32, 1, 128, 16, 8192) == starts(32, w) + w * 2 * rec(32, 128)
+    w = waves(4)  # one query head per kv head, head_dim 64: the vector-ALU loop of two waves per SIMD
+    assert pkv.decode_workspace_size(4, 4, 4, 64, 16, 3) == starts(4, w) + w * 2 * rec(1, 64)
+    # the single mixed launch: one four-wave workgroup per compute unit
+    w = waves(1)
+    assert pkv.mixed_workspace_size(40, 32, 1, 128, 16) == starts(40, w) + w * 2 * rec(32, 128)
     # fixed partitions: one record per (sequence, kv head, partition); none when one partition fits all
     assert pkv.decode_workspace_size(8, 8, 8, 64, 16, 32, partition_size=512) == 0
     assert pkv.decode_workspace_size(8, 8, 8, 64, 16, 33, partition_size=512) == 8 * 8 * 2 * rec(1, 64)
@@ -204,7 +214,6 @@ def test_mixed_empty_is_a_no_op_and_workspace_size():
     assert _mixed(num_segs=0, out=None, workspace=None) == 0
     assert _mixed(total_q=0, max_q_len=0, query=None) == 0
     # the balanced-split workspace of the decode call for that many sequences
-    assert pkv.mixed_workspace_size(40, 32, 1, 128, 16) == pkv.decode_workspace_size(40, 32, 1, 128, 16, 1, 0)
     assert pkv.mixed_workspace_size(0, 32, 1, 128, 16) == 0
 
 
