@@ -150,6 +150,29 @@ int paged_attention_decode(void* out, const void* query, const void* key_cache, 
                            size_t workspace_bytes, void* stream);
 
 /*
+ * paged_attention_decode_static -- paged_attention_decode without a workspace
+ * argument, for callers that cannot allocate device memory: code under HIP graph
+ * capture, serving loops that must not call the allocator, harnesses that forbid it.
+ *
+ * Same arguments (minus workspace / workspace_bytes), same kernels, same result bit
+ * for bit as paged_attention_decode.  The scratch it needs comes from a device
+ * array of PKV_STATIC_SCRATCH_BYTES inside the library: each GPU the library runs
+ * on holds its own copy from the first call on it until the process ends.  The call
+ * allocates and frees nothing.
+ *   - A call whose scratch need (pkv_decode_workspace_size of the same arguments)
+ *     exceeds PKV_STATIC_SCRATCH_BYTES returns PKV_ERR_WORKSPACE and launches
+ *     nothing; use paged_attention_decode with a workspace for it.
+ *   - Every call on one GPU shares that GPU's array, and nothing in it has to start
+ *     at any particular value.  Calls that overlap in time on one GPU (other
+ *     streams, other host threads) race on it: order them.
+ */
+#define PKV_STATIC_SCRATCH_BYTES ((size_t)64 << 20)
+int paged_attention_decode_static(void* out, const void* query, const void* key_cache, const void* value_cache,
+                                  const int32_t* block_tables, const int32_t* context_lens, int num_seqs,
+                                  int num_q_heads, int num_kv_heads, int head_dim, int block_size, int num_blocks,
+                                  int max_blocks_per_seq, float scale, int dtype, int partition_size, void* stream);
+
+/*
  * paged_attention_chunked -- [P2] sections 1.4 and 2.1 (a long prompt is cut into
  * chunks that run in a flattened batch); [P3] section 3.1 (causal attention).
  *

@@ -14,6 +14,7 @@ from .pkv import (  # noqa: F401
     mixed_workspace_size,
     paged_attention_chunked,
     paged_attention_decode,
+    paged_attention_decode_static,
     paged_attention_mixed,
     read_probe,
     reshape_and_cache,

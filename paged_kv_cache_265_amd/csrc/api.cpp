@@ -15,6 +15,8 @@
 
 #include "internal.h"
 
+static_assert(PKV_STATIC_SCRATCH_BYTES == pkv::kStaticScratchBytes, "header and library agree on the static scratch");
+
 namespace {
 thread_local char g_msg[512] = "";
 }  // namespace
@@ -186,11 +188,13 @@ size_t pkv_decode_workspace_size(int num_seqs, int num_q_heads, int num_kv_heads
 
 namespace {
 
-// paged_attention_decode: validation, workspace check, launch
+// paged_attention_decode with its workspace either given by the caller or, with
+// use_static, the library's per-device static scratch (paged_attention_decode_static).
 int decode_call(const char* fn, void* out, const void* query, const void* key_cache, const void* value_cache,
                 const int32_t* block_tables, const int32_t* context_lens, int num_seqs, int num_q_heads,
                 int num_kv_heads, int head_dim, int block_size, int num_blocks, int max_blocks_per_seq, float scale,
-                int dtype, int partition_size, void* workspace, size_t workspace_bytes, void* stream) {
+                int dtype, int partition_size, void* workspace, size_t workspace_bytes, bool use_static,
+                void* stream) {
     int rc;
     if ((rc = check_pool(fn, num_kv_heads, head_dim, block_size, num_blocks, dtype)) != PKV_OK) return rc;
     if ((rc = check_heads(fn, num_q_heads, num_kv_heads)) != PKV_OK) return rc;
@@ -219,11 +223,25 @@ int decode_call(const char* fn, void* out, const void* query, const void* key_ca
     long long waves = 0;
     const size_t need = decode_need(num_seqs, num_q_heads, num_kv_heads, head_dim, block_size, max_blocks_per_seq,
                                     partition_size, dtype, path, &waves);
-    if (need > 0 && (!workspace || workspace_bytes < need))
-        return set_error(PKV_ERR_WORKSPACE, "%s: workspace of %zu bytes needed, %zu given", fn, need,
-                         workspace ? workspace_bytes : (size_t)0);
-    if (need > 0 && !aligned(workspace, 16))
-        return set_error(PKV_ERR_INVALID, "%s: workspace must be 16-byte aligned", fn);
+    if (use_static) {
+        if (need > pkv::kStaticScratchBytes)
+            return set_error(PKV_ERR_WORKSPACE,
+                             "%s: this call needs %zu bytes of scratch, beyond the %zu bytes of the static scratch; "
+                             "use paged_attention_decode with a workspace",
+                             fn, need, pkv::kStaticScratchBytes);
+        workspace = nullptr;
+        if (need > 0) {
+            hipError_t e = pkv::static_scratch_address(&workspace);
+            if (e != hipSuccess)
+                return set_error(PKV_ERR_HIP, "%s: static scratch lookup failed: %s", fn, hipGetErrorString(e));
+        }
+    } else {
+        if (need > 0 && (!workspace || workspace_bytes < need))
+            return set_error(PKV_ERR_WORKSPACE, "%s: workspace of %zu bytes needed, %zu given", fn, need,
+                             workspace ? workspace_bytes : (size_t)0);
+        if (need > 0 && !aligned(workspace, 16))
+            return set_error(PKV_ERR_INVALID, "%s: workspace must be 16-byte aligned", fn);
+    }
 
     pkv::DecodeParams p;
     p.out = out;
@@ -270,7 +288,16 @@ int paged_attention_decode(void* out, const void* query, const void* key_cache, 
                            size_t workspace_bytes, void* stream) {
     return decode_call("paged_attention_decode", out, query, key_cache, value_cache, block_tables, context_lens,
                        num_seqs, num_q_heads, num_kv_heads, head_dim, block_size, num_blocks, max_blocks_per_seq,
-                       scale, dtype, partition_size, workspace, workspace_bytes, stream);
+                       scale, dtype, partition_size, workspace, workspace_bytes, false, stream);
+}
+
+int paged_attention_decode_static(void* out, const void* query, const void* key_cache, const void* value_cache,
+                                  const int32_t* block_tables, const int32_t* context_lens, int num_seqs,
+                                  int num_q_heads, int num_kv_heads, int head_dim, int block_size, int num_blocks,
+                                  int max_blocks_per_seq, float scale, int dtype, int partition_size, void* stream) {
+    return decode_call("paged_attention_decode_static", out, query, key_cache, value_cache, block_tables,
+                       context_lens, num_seqs, num_q_heads, num_kv_heads, head_dim, block_size, num_blocks,
+                       max_blocks_per_seq, scale, dtype, partition_size, nullptr, 0, true, stream);
 }
 
 int paged_attention_chunked(void* out, const void* query, const int32_t* cu_q_lens, int num_segs, int total_q,

@@ -110,6 +110,11 @@ hipError_t launch_reshape_and_cache(const CacheParams& p, int kind, hipStream_t 
 hipError_t launch_copy_blocks(const CopyParams& p, int num_layers, hipStream_t stream);
 hipError_t launch_read_probe(const void* buf, size_t bytes, void* sink, hipStream_t stream);
 
+// Size of the device array behind paged_attention_decode_static (one copy per GPU),
+// and the address of the current device's copy (looked up once per device).
+constexpr size_t kStaticScratchBytes = (size_t)64 << 20;
+hipError_t static_scratch_address(void** ptr);
+
 // thread-local message of pkv_last_error(); returns code
 int set_error(int code, const char* fmt, ...);
 

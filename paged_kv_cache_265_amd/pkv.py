@@ -29,6 +29,7 @@ SYMBOLS = (
     "pkv_decode_partition_size",
     "pkv_decode_workspace_size",
     "paged_attention_decode",
+    "paged_attention_decode_static",
     "paged_attention_chunked",
     "paged_attention_mixed",
     "pkv_mixed_workspace_size",
@@ -66,6 +67,8 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.pkv_decode_workspace_size.restype = Z
     lib.paged_attention_decode.argtypes = [P, P, P, P, P, P, I, I, I, I, I, I, I, F, I, I, P, Z, P]
     lib.paged_attention_decode.restype = I
+    lib.paged_attention_decode_static.argtypes = [P, P, P, P, P, P, I, I, I, I, I, I, I, F, I, I, P]
+    lib.paged_attention_decode_static.restype = I
     lib.paged_attention_chunked.argtypes = [P, P, P, I, I, I, P, P, P, P, I, I, I, I, I, I, F, I, P]
     lib.paged_attention_chunked.restype = I
     lib.paged_attention_mixed.argtypes = [P, P, P, I, I, I, P, P, P, P, I, I, I, I, I, I, F, I, P, Z, P]
@@ -160,6 +163,26 @@ def paged_attention_decode(out: torch.Tensor, query: torch.Tensor, key_cache: to
     rc = load_library().paged_attention_decode(
         _ptr(out), _ptr(query), _ptr(key_cache), _ptr(value_cache), _ptr(block_tables), _ptr(context_lens), S, Hq,
         Hkv, D, BS, NB, MB, float(scale), dt, int(partition_size), _ptr(workspace), ws_bytes, _stream(stream))
+    _check(rc)
+    return out
+
+
+STATIC_SCRATCH_BYTES = 64 << 20  # PKV_STATIC_SCRATCH_BYTES
+
+
+def paged_attention_decode_static(out: torch.Tensor, query: torch.Tensor, key_cache: torch.Tensor,
+                                  value_cache: torch.Tensor, block_tables: torch.Tensor, context_lens: torch.Tensor,
+                                  scale: float, partition_size: int = 0, stream=None) -> torch.Tensor:
+    """paged_attention_decode without a workspace: the library's static per-device
+    scratch holds the partial records, so nothing is allocated (see include/pkv.h)."""
+    _contig(out, query, key_cache, value_cache, block_tables, context_lens)
+    S, Hq, D = query.shape
+    NB, Hkv, BS, _ = key_cache.shape
+    MB = block_tables.shape[1] if block_tables.dim() == 2 else 0
+    dt = _dtype(out, query, key_cache, value_cache)
+    rc = load_library().paged_attention_decode_static(
+        _ptr(out), _ptr(query), _ptr(key_cache), _ptr(value_cache), _ptr(block_tables), _ptr(context_lens), S, Hq,
+        Hkv, D, BS, NB, MB, float(scale), dt, int(partition_size), _stream(stream))
     _check(rc)
     return out
 

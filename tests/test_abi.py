@@ -144,6 +144,32 @@ def test_decode_rejects(over, code):
     assert pkv.load_library().pkv_last_error()  # a message explains it
 
 
+def _decode_static(**over):
+    a = dict(out=FAKE, query=FAKE, key_cache=FAKE, value_cache=FAKE, block_tables=FAKE, context_lens=FAKE,
+             num_seqs=2, num_q_heads=8, num_kv_heads=2, head_dim=128, block_size=16, num_blocks=10,
+             max_blocks_per_seq=4, scale=0.1, dtype=2, partition_size=0, stream=None)
+    a.update(over)
+    return pkv.load_library().paged_attention_decode_static(*a.values())
+
+
+@pytest.mark.parametrize("over,code", [o for o in DECODE_BAD if "workspace" not in o[0] and
+                                       o[0].get("partition_size") != 32])
+def test_decode_static_rejects_like_decode(over, code):
+    assert _decode_static(**over) == code
+    assert pkv.load_library().pkv_last_error()
+
+
+def test_decode_static_rejects_a_need_beyond_the_static_scratch():
+    """1024 long MQA sequences in 512-token partitions need ~4.4 GB of records: refused
+    on the host, before any device work."""
+    over = dict(num_seqs=1024, num_q_heads=32, num_kv_heads=1, max_blocks_per_seq=8192, partition_size=512)
+    need = pkv.decode_workspace_size(1024, 32, 1, 128, 16, 8192, 512)
+    assert need > pkv.pkv.STATIC_SCRATCH_BYTES
+    assert _decode_static(**over) == pkv.pkv.ERR_WORKSPACE
+    assert b"static scratch" in pkv.load_library().pkv_last_error()
+    assert _decode_static(num_seqs=0, out=None) == 0
+
+
 def test_decode_empty_batch_is_a_no_op():
     assert _decode(num_seqs=0, out=None, query=None) == 0
 
