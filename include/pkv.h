@@ -61,11 +61,13 @@
  *  - Errors: arguments are validated on the host before anything is launched; an
  *    invalid argument returns a negative code and launches nothing.  A launch
  *    failure returns PKV_ERR_HIP.  pkv_last_error() gives a message.
- *  - Device-side contract (not checked): block ids in tables and block_mapping are
- *    in [0, NB); context_lens[i] <= MB * BS; slots are unique and < NB * BS; the
- *    copy_blocks destination set has no duplicates and is disjoint from its
- *    source set; outputs do not alias inputs.  Breaking it reads or writes out of
- *    bounds.
+ *  - Device-side contract (checked only with PKV_DEBUG_CHECKS=1, see below): block
+ *    ids in tables and block_mapping are in [0, NB); 0 <= context_lens[i] <= MB * BS;
+ *    cu_q_lens starts at 0, never decreases, ends at total_q, and no segment has
+ *    more than max_q_len rows or more rows than context tokens; slots are unique and
+ *    < NB * BS; the copy_blocks destination set has no duplicates and is disjoint
+ *    from its source set; outputs do not alias inputs.  Unchecked, breaking it reads
+ *    or writes out of bounds.
  *  - Pointers to query/out/caches/key/value must be 16-byte aligned.
  */
 #ifndef PKV_H
@@ -85,7 +87,8 @@ enum pkv_status {
     PKV_ERR_INVALID = -1,     /* null pointer, bad size, Hq % Hkv != 0, bad scale, misaligned pointer */
     PKV_ERR_UNSUPPORTED = -2, /* head_dim, block_size or dtype outside the supported set */
     PKV_ERR_WORKSPACE = -3,   /* workspace missing or smaller than pkv_decode_workspace_size() */
-    PKV_ERR_HIP = -4          /* the HIP runtime refused a launch */
+    PKV_ERR_HIP = -4,         /* the HIP runtime refused a launch */
+    PKV_ERR_CONTRACT = -6     /* PKV_DEBUG_CHECKS=1: the device-side contract is broken */
 };
 
 /* Library version as major * 10000 + minor * 100 + patch. */
@@ -112,7 +115,10 @@ int pkv_decode_partition_size(int num_seqs, int num_q_heads, int num_kv_heads, i
  *   partition_size > 0: one such record per (sequence, query head, partition);
  *     zero when every sequence fits one partition (max_blocks_per_seq *
  *     block_size <= partition_size).
- * Returns 0 on invalid arguments as well; the decode call then reports the error. */
+ * 0 means no workspace is needed (num_seqs == 0 included).  Invalid arguments (those
+ * paged_attention_decode would reject as PKV_ERR_INVALID) return PKV_SIZE_INVALID,
+ * with pkv_last_error() saying why. */
+#define PKV_SIZE_INVALID ((size_t)-1)
 size_t pkv_decode_workspace_size(int num_seqs, int num_q_heads, int num_kv_heads, int head_dim, int block_size,
                                  int max_blocks_per_seq, int partition_size);
 
@@ -213,8 +219,10 @@ int paged_attention_mixed(void* out, const void* query, const int32_t* cu_q_lens
                           int block_size, int num_blocks, int max_blocks_per_seq, float scale, int dtype,
                           void* workspace, size_t workspace_bytes, void* stream);
 
-/* Bytes of workspace paged_attention_mixed needs (the balanced-split workspace of
- * paged_attention_decode for num_segs sequences); 0 on invalid arguments. */
+/* Bytes of workspace paged_attention_mixed needs: the balanced-split layout of
+ * paged_attention_decode for num_segs sequences and one four-wave workgroup of decode
+ * waves per compute unit of the current device.  PKV_SIZE_INVALID on invalid
+ * arguments. */
 size_t pkv_mixed_workspace_size(int num_segs, int num_q_heads, int num_kv_heads, int head_dim, int block_size);
 
 /*
@@ -259,6 +267,80 @@ int copy_blocks(void* const* key_caches, void* const* value_caches, int num_laye
  *          keeps the loads from being optimised away.
  */
 int pkv_read_probe(const void* buf, size_t bytes, void* sink, void* stream);
+
+/*
+ * Checking the device-side contract.
+ *
+ * With the environment variable PKV_DEBUG_CHECKS set to 1 (read at every call),
+ * paged_attention_decode(_static), paged_attention_chunked, paged_attention_mixed,
+ * reshape_and_cache and copy_blocks first enqueue a pre-pass over their tables,
+ * context lengths, query lengths, slots or copy pairs (nothing else is read), and
+ * every kernel of the call returns at once if it found a violation, so nothing is
+ * read or written out of bounds.  The call then waits for its stream and returns
+ * PKV_ERR_CONTRACT, pkv_last_error() naming the first violation.  Checked calls
+ * synchronise, are serialised across the process, and must not be captured in a
+ * graph; unchecked calls (the default) are unaffected.
+ *
+ * A verdict word packs a violation as (index << 32) | (sub-index << 8) | code,
+ * with index the sequence / segment / token / pair and sub-index the logical block
+ * (PKV_BAD_BLOCK_ID), the side of a pair (PKV_BAD_COPY_BLOCK: 0 source, 1
+ * destination) or the broken condition (PKV_BAD_QUERY_LENS: 0 cu_q_lens[0] != 0,
+ * 1 rows < 0 or > max_q_len, 2 rows > context, 3 last entry != total_q); the
+ * verdict of a whole check is the smallest such word, PKV_CONTRACT_OK if none.
+ */
+#define PKV_CONTRACT_OK (~(uint64_t)0)
+enum pkv_contract_code {
+    PKV_BAD_CONTEXT_LEN = 1,    /* context_lens[s] < 0 or > MB * BS */
+    PKV_BAD_BLOCK_ID = 2,       /* block_tables[s][b] outside [0, NB), b < ceil(ctx / BS) */
+    PKV_BAD_QUERY_LENS = 3,     /* cu_q_lens breaks its rules */
+    PKV_BAD_SLOT = 4,           /* slot_mapping[i] >= NB * BS */
+    PKV_DUPLICATE_SLOT = 5,     /* slot_mapping[i] equals an earlier non-negative slot */
+    PKV_BAD_COPY_BLOCK = 6,     /* a source or destination outside [0, NB) */
+    PKV_DUPLICATE_COPY_DST = 7, /* a destination repeats an earlier pair's */
+    PKV_COPY_DST_IS_SRC = 8     /* a destination is also a source */
+};
+
+/* The same checks as calls of their own.  The pkv_check_* calls take device arrays,
+ * run the pre-pass on `stream`, wait for it and store the verdict in *verdict (host
+ * memory); they return PKV_OK (whatever the verdict), PKV_ERR_INVALID for bad sizes
+ * or null pointers, PKV_ERR_HIP on a runtime failure.  The *_host variants take host
+ * arrays, run the very same item checks on the CPU and return the verdict.
+ *   tables: rows x max_blocks_per_seq block_tables and rows context_lens; with
+ *     cu_q_lens (rows + 1 entries) non-NULL the chunked/mixed query-length rules too. */
+int pkv_check_tables(const int32_t* block_tables, const int32_t* context_lens, const int32_t* cu_q_lens, int num_rows,
+                     int max_blocks_per_seq, int block_size, int num_blocks, int total_q, int max_q_len,
+                     uint64_t* verdict, void* stream);
+int pkv_check_slots(const int64_t* slot_mapping, int num_tokens, int block_size, int num_blocks, uint64_t* verdict,
+                    void* stream);
+int pkv_check_copies(const int64_t* block_mapping, int num_pairs, int num_blocks, uint64_t* verdict, void* stream);
+uint64_t pkv_check_tables_host(const int32_t* block_tables, const int32_t* context_lens, const int32_t* cu_q_lens,
+                               int num_rows, int max_blocks_per_seq, int block_size, int num_blocks, int total_q,
+                               int max_q_len);
+uint64_t pkv_check_slots_host(const int64_t* slot_mapping, int num_tokens, int block_size, int num_blocks);
+uint64_t pkv_check_copies_host(const int64_t* block_mapping, int num_pairs, int num_blocks);
+
+/*
+ * pkv_decode_variant -- test and measurement hook, not part of the attention path's
+ * interface: paged_attention_decode with its inner loop and prefetch depth chosen
+ * by the caller instead of by the library, so that every loop can be compared with
+ * the others on the same inputs.  Same arguments, result and conventions as
+ * paged_attention_decode, plus
+ *   inner_loop: 0 the library's choice, 1 the vector-ALU loop, 2 the matrix-core loop
+ *               (16-bit types only; PKV_ERR_UNSUPPORTED for fp32);
+ *   ring:       0 the loop's own prefetch depth, 2 a two-tile ring (one block in
+ *               flight; used by the balanced split only).
+ * Its workspace is pkv_decode_variant_workspace_size(...) bytes (the same arguments
+ * as pkv_decode_workspace_size plus dtype, inner_loop and ring; PKV_SIZE_INVALID on
+ * invalid ones).
+ */
+int pkv_decode_variant(void* out, const void* query, const void* key_cache, const void* value_cache,
+                       const int32_t* block_tables, const int32_t* context_lens, int num_seqs, int num_q_heads,
+                       int num_kv_heads, int head_dim, int block_size, int num_blocks, int max_blocks_per_seq,
+                       float scale, int dtype, int partition_size, void* workspace, size_t workspace_bytes,
+                       int inner_loop, int ring, void* stream);
+size_t pkv_decode_variant_workspace_size(int num_seqs, int num_q_heads, int num_kv_heads, int head_dim,
+                                         int block_size, int max_blocks_per_seq, int partition_size, int dtype,
+                                         int inner_loop, int ring);
 
 /* Fixed text for a status code. */
 const char* pkv_error_string(int status);

@@ -18,7 +18,7 @@ HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
 
 # the three decode units (one per block size) take longest: they go first
-SOURCES = ["decode.hip", "decode_bs8.hip", "decode_bs32.hip", "mixed.hip", "chunked.hip", "cache_ops.hip", "probe.hip", "static_scratch.hip",
+SOURCES = ["decode.hip", "decode_bs8.hip", "decode_bs32.hip", "mixed.hip", "chunked.hip", "cache_ops.hip", "probe.hip", "static_scratch.hip", "contract.hip",
            "api.cpp", "block_manager.cpp"]
 
 # Packed fp32 instructions are kept out of the generated code on purpose.  The

@@ -39,6 +39,19 @@ int hip_fail(hipError_t e, const char* what) {
     return set_error(PKV_ERR_HIP, "%s: launch failed: %s", what, hipGetErrorString(e));
 }
 
+// End of a call made with the contract pre-pass: wait for the verdict and turn a
+// violation into PKV_ERR_CONTRACT.
+int finish_checked(const char* fn, pkv::DebugChecks& dbg) {
+    if (!dbg.on()) return PKV_OK;
+    uint64_t v = PKV_CONTRACT_OK;
+    const hipError_t e = dbg.finish(&v);
+    if (e != hipSuccess) return set_error(PKV_ERR_HIP, "%s: contract check failed: %s", fn, hipGetErrorString(e));
+    if (v == PKV_CONTRACT_OK) return PKV_OK;
+    char what[256];
+    pkv::describe_violation(v, what, sizeof what);
+    return set_error(PKV_ERR_CONTRACT, "%s: %s", fn, what);
+}
+
 bool aligned(const void* p, size_t a) { return ((uintptr_t)p & (a - 1)) == 0; }
 
 bool dtype_ok(int dt) { return dt == PKV_F32 || dt == PKV_F16 || dt == PKV_BF16; }
@@ -84,10 +97,10 @@ size_t split_prefix_bytes(int num_seqs, long long waves) {
 // Waves the balanced split launches at most on the current device: every compute
 // unit holds at most kSimdsPerCu x (waves per SIMD of the inner loop); kind < 0
 // takes the largest over the three element types.
-long long split_wave_bound(int kind, int G, int D, int path) {
+long long split_wave_bound(int kind, int G, int D, int path, int ring) {
     int per_simd = 0;
     for (int k = PKV_F32; k <= PKV_BF16; ++k)
-        if (kind < 0 || kind == k) per_simd = std::max(per_simd, pkv::split_waves_per_simd(k, G, D, path));
+        if (kind < 0 || kind == k) per_simd = std::max(per_simd, pkv::split_waves_per_simd(k, G, D, path, ring));
     const long long w = (long long)pkv::device_compute_units() * pkv::kSimdsPerCu * per_simd;
     return std::min<long long>(w, pkv::kMaxSplitWaves);
 }
@@ -114,30 +127,29 @@ void record_shape(int G, long long* heads_per_kv, int* cap_max) {
     *cap_max = cap;
 }
 
-// Decode path override for testing and measurement: PKV_DECODE_PATH=valu|mfma.
-int decode_path() {
-    const char* e = std::getenv("PKV_DECODE_PATH");
-    if (!e || !*e || !std::strcmp(e, "auto")) return 0;
-    if (!std::strcmp(e, "valu")) return 1;
-    if (!std::strcmp(e, "mfma")) return 2;
-    return -1;
-}
 
 // Workspace bytes of a decode (see pkv_decode_workspace_size); kind < 0: enough for
 // every element type.  *waves: the wave bound the balanced split's layout uses.
+// PKV_SIZE_INVALID (with a message) for arguments no decode call would accept.
 size_t decode_need(int num_seqs, int num_q_heads, int num_kv_heads, int head_dim, int block_size,
-                   int max_blocks_per_seq, int partition_size, int kind, int path, long long* waves) {
+                   int max_blocks_per_seq, int partition_size, int kind, int path, int ring, long long* waves) {
     *waves = 0;
-    if (num_seqs <= 0 || num_q_heads <= 0 || num_kv_heads <= 0 || num_q_heads % num_kv_heads != 0 ||
-        head_dim <= 0 || block_size <= 0 || max_blocks_per_seq <= 0 || !partition_ok(partition_size, block_size))
-        return 0;
+    if (num_seqs < 0 || num_q_heads <= 0 || num_kv_heads <= 0 || num_q_heads % num_kv_heads != 0 ||
+        head_dim <= 0 || block_size <= 0 || max_blocks_per_seq <= 0 || !partition_ok(partition_size, block_size) ||
+        path < 0 || path > 2 || (ring != 0 && ring != 2)) {
+        set_error(PKV_ERR_INVALID,
+                  "workspace size: invalid arguments (num_seqs >= 0, positive head counts with num_q_heads a multiple "
+                  "of num_kv_heads, positive sizes, partition_size 0 or a multiple of block_size and 16)");
+        return PKV_SIZE_INVALID;
+    }
+    if (num_seqs == 0) return 0;
     const int G = num_q_heads / num_kv_heads;
     long long heads_per_kv = 0;
     int cap = 0;
     record_shape(G, &heads_per_kv, &cap);
     const size_t per_head = ((size_t)head_dim + 2) * sizeof(float);
     if (partition_size == 0) {
-        *waves = split_wave_bound(kind, G, head_dim, path);
+        *waves = split_wave_bound(kind, G, head_dim, path, ring);
         return split_prefix_bytes(num_seqs, *waves) + (size_t)*waves * 2 * cap * per_head;
     }
     const int mp = max_parts(max_blocks_per_seq, block_size, partition_size);
@@ -159,6 +171,7 @@ const char* pkv_error_string(int status) {
     case PKV_ERR_WORKSPACE: return "workspace missing or too small";
     case PKV_ERR_HIP: return "HIP launch failure";
     case PKV_ERR_NO_BLOCKS: return "no free block in the pool";
+    case PKV_ERR_CONTRACT: return "device-side contract broken (PKV_DEBUG_CHECKS)";
     default: return "unknown status";
     }
 }
@@ -181,7 +194,7 @@ size_t pkv_decode_workspace_size(int num_seqs, int num_q_heads, int num_kv_heads
                                  int max_blocks_per_seq, int partition_size) {
     long long waves = 0;
     return decode_need(num_seqs, num_q_heads, num_kv_heads, head_dim, block_size, max_blocks_per_seq, partition_size,
-                       -1, 0, &waves);
+                       -1, 0, 0, &waves);
 }
 
 }  // extern "C"
@@ -193,8 +206,8 @@ namespace {
 int decode_call(const char* fn, void* out, const void* query, const void* key_cache, const void* value_cache,
                 const int32_t* block_tables, const int32_t* context_lens, int num_seqs, int num_q_heads,
                 int num_kv_heads, int head_dim, int block_size, int num_blocks, int max_blocks_per_seq, float scale,
-                int dtype, int partition_size, void* workspace, size_t workspace_bytes, bool use_static,
-                void* stream) {
+                int dtype, int partition_size, void* workspace, size_t workspace_bytes, bool use_static, int path,
+                int ring, void* stream) {
     int rc;
     if ((rc = check_pool(fn, num_kv_heads, head_dim, block_size, num_blocks, dtype)) != PKV_OK) return rc;
     if ((rc = check_heads(fn, num_q_heads, num_kv_heads)) != PKV_OK) return rc;
@@ -206,8 +219,8 @@ int decode_call(const char* fn, void* out, const void* query, const void* key_ca
     if (!partition_ok(partition_size, block_size))
         return set_error(PKV_ERR_INVALID, "%s: partition_size %d must be 0 or a positive multiple of block_size and 16",
                          fn, partition_size);
-    const int path = decode_path();
-    if (path < 0) return set_error(PKV_ERR_INVALID, "%s: PKV_DECODE_PATH must be auto, valu or mfma", fn);
+    if (path < 0 || path > 2 || (ring != 0 && ring != 2))
+        return set_error(PKV_ERR_INVALID, "%s: inner_loop must be 0, 1 or 2 and ring 0 or 2", fn);
     if (path == 2 && dtype == PKV_F32)
         return set_error(PKV_ERR_UNSUPPORTED, "%s: the matrix-core path takes 16-bit types only", fn);
     if (num_seqs == 0) return PKV_OK;
@@ -222,7 +235,7 @@ int decode_call(const char* fn, void* out, const void* query, const void* key_ca
     if (grid > 0x7fffffffLL) return set_error(PKV_ERR_INVALID, "%s: problem too large for one launch", fn);
     long long waves = 0;
     const size_t need = decode_need(num_seqs, num_q_heads, num_kv_heads, head_dim, block_size, max_blocks_per_seq,
-                                    partition_size, dtype, path, &waves);
+                                    partition_size, dtype, path, ring, &waves);
     if (use_static) {
         if (need > pkv::kStaticScratchBytes)
             return set_error(PKV_ERR_WORKSPACE,
@@ -243,7 +256,12 @@ int decode_call(const char* fn, void* out, const void* query, const void* key_ca
             return set_error(PKV_ERR_INVALID, "%s: workspace must be 16-byte aligned", fn);
     }
 
+    pkv::DebugChecks dbg((hipStream_t)stream, pkv::debug_checks_requested());
+    (void)dbg.tables(block_tables, context_lens, nullptr, num_seqs, max_blocks_per_seq, block_size, num_blocks, 0, 0);
+    if (dbg.error() != hipSuccess) return hip_fail(dbg.error(), fn);
+
     pkv::DecodeParams p;
+    p.guard = dbg.guard();
     p.out = out;
     p.q = query;
     p.kc = key_cache;
@@ -272,9 +290,9 @@ int decode_call(const char* fn, void* out, const void* query, const void* key_ca
     p.part_tokens = partition_size;
     p.max_parts = mp;
     p.scale_log2 = scale * pkv::kLog2eHost;
-    hipError_t e = pkv::launch_decode_path(p, dtype, path, (hipStream_t)stream);
+    hipError_t e = pkv::launch_decode_path(p, dtype, path, ring, (hipStream_t)stream);
     if (e != hipSuccess) return hip_fail(e, fn);
-    return PKV_OK;
+    return finish_checked(fn, dbg);
 }
 
 }  // namespace
@@ -288,7 +306,25 @@ int paged_attention_decode(void* out, const void* query, const void* key_cache, 
                            size_t workspace_bytes, void* stream) {
     return decode_call("paged_attention_decode", out, query, key_cache, value_cache, block_tables, context_lens,
                        num_seqs, num_q_heads, num_kv_heads, head_dim, block_size, num_blocks, max_blocks_per_seq,
-                       scale, dtype, partition_size, workspace, workspace_bytes, false, stream);
+                       scale, dtype, partition_size, workspace, workspace_bytes, false, 0, 0, stream);
+}
+
+int pkv_decode_variant(void* out, const void* query, const void* key_cache, const void* value_cache,
+                       const int32_t* block_tables, const int32_t* context_lens, int num_seqs, int num_q_heads,
+                       int num_kv_heads, int head_dim, int block_size, int num_blocks, int max_blocks_per_seq,
+                       float scale, int dtype, int partition_size, void* workspace, size_t workspace_bytes,
+                       int inner_loop, int ring, void* stream) {
+    return decode_call("pkv_decode_variant", out, query, key_cache, value_cache, block_tables, context_lens,
+                       num_seqs, num_q_heads, num_kv_heads, head_dim, block_size, num_blocks, max_blocks_per_seq,
+                       scale, dtype, partition_size, workspace, workspace_bytes, false, inner_loop, ring, stream);
+}
+
+size_t pkv_decode_variant_workspace_size(int num_seqs, int num_q_heads, int num_kv_heads, int head_dim,
+                                         int block_size, int max_blocks_per_seq, int partition_size, int dtype,
+                                         int inner_loop, int ring) {
+    long long waves = 0;
+    return decode_need(num_seqs, num_q_heads, num_kv_heads, head_dim, block_size, max_blocks_per_seq, partition_size,
+                       dtype, inner_loop, ring, &waves);
 }
 
 int paged_attention_decode_static(void* out, const void* query, const void* key_cache, const void* value_cache,
@@ -297,7 +333,7 @@ int paged_attention_decode_static(void* out, const void* query, const void* key_
                                   int max_blocks_per_seq, float scale, int dtype, int partition_size, void* stream) {
     return decode_call("paged_attention_decode_static", out, query, key_cache, value_cache, block_tables,
                        context_lens, num_seqs, num_q_heads, num_kv_heads, head_dim, block_size, num_blocks,
-                       max_blocks_per_seq, scale, dtype, partition_size, nullptr, 0, true, stream);
+                       max_blocks_per_seq, scale, dtype, partition_size, nullptr, 0, true, 0, 0, stream);
 }
 
 int paged_attention_chunked(void* out, const void* query, const int32_t* cu_q_lens, int num_segs, int total_q,
@@ -327,7 +363,12 @@ int paged_attention_chunked(void* out, const void* query, const int32_t* cu_q_le
     const long long tiles = ((long long)max_q_len * G + 127) / 128;
     if (tiles * num_kv_heads * num_segs > 0x7fffffffLL)
         return set_error(PKV_ERR_INVALID, "%s: problem too large for one launch", fn);
+    pkv::DebugChecks dbg((hipStream_t)stream, pkv::debug_checks_requested());
+    (void)dbg.tables(block_tables, context_lens, cu_q_lens, num_segs, max_blocks_per_seq, block_size, num_blocks, total_q,
+               max_q_len);
+    if (dbg.error() != hipSuccess) return hip_fail(dbg.error(), fn);
     pkv::ChunkedParams p;
+    p.guard = dbg.guard();
     p.out = out;
     p.q = query;
     p.cu_q_lens = cu_q_lens;
@@ -348,13 +389,16 @@ int paged_attention_chunked(void* out, const void* query, const int32_t* cu_q_le
     p.scale_log2 = scale * pkv::kLog2eHost;
     hipError_t e = pkv::launch_chunked(p, dtype, (hipStream_t)stream);
     if (e != hipSuccess) return hip_fail(e, fn);
-    return PKV_OK;
+    return finish_checked(fn, dbg);
 }
 
 size_t pkv_mixed_workspace_size(int num_segs, int num_q_heads, int num_kv_heads, int head_dim, int block_size) {
-    if (num_segs <= 0 || num_q_heads <= 0 || num_kv_heads <= 0 || num_q_heads % num_kv_heads != 0 ||
-        head_dim <= 0 || block_size <= 0)
-        return 0;
+    if (num_segs < 0 || num_q_heads <= 0 || num_kv_heads <= 0 || num_q_heads % num_kv_heads != 0 ||
+        head_dim <= 0 || block_size <= 0) {
+        set_error(PKV_ERR_INVALID, "pkv_mixed_workspace_size: invalid arguments");
+        return PKV_SIZE_INVALID;
+    }
+    if (num_segs == 0) return 0;
     long long heads_per_kv = 0;
     int cap = 0;
     record_shape(num_q_heads / num_kv_heads, &heads_per_kv, &cap);
@@ -396,7 +440,12 @@ int paged_attention_mixed(void* out, const void* query, const int32_t* cu_q_lens
                          workspace ? workspace_bytes : (size_t)0);
     if (!aligned(workspace, 16)) return set_error(PKV_ERR_INVALID, "%s: workspace must be 16-byte aligned", fn);
 
+    pkv::DebugChecks dbg((hipStream_t)stream, pkv::debug_checks_requested());
+    (void)dbg.tables(block_tables, context_lens, cu_q_lens, num_segs, max_blocks_per_seq, block_size, num_blocks, total_q,
+               max_q_len);
+    if (dbg.error() != hipSuccess) return hip_fail(dbg.error(), fn);
     pkv::ChunkedParams c;
+    c.guard = dbg.guard();
     c.out = out;
     c.q = query;
     c.cu_q_lens = cu_q_lens;
@@ -417,6 +466,7 @@ int paged_attention_mixed(void* out, const void* query, const int32_t* cu_q_lens
     c.scale_log2 = scale * pkv::kLog2eHost;
 
     pkv::DecodeParams d;
+    d.guard = dbg.guard();
     d.out = out;
     d.q = query;
     d.kc = key_cache;
@@ -441,7 +491,7 @@ int paged_attention_mixed(void* out, const void* query, const int32_t* cu_q_lens
     d.scale_log2 = c.scale_log2;
     hipError_t e = pkv::launch_mixed(d, c, dtype, (hipStream_t)stream);
     if (e != hipSuccess) return hip_fail(e, fn);
-    return PKV_OK;
+    return finish_checked(fn, dbg);
 }
 
 int reshape_and_cache(const void* key, const void* value, void* key_cache, void* value_cache,
@@ -457,7 +507,11 @@ int reshape_and_cache(const void* key, const void* value, void* key_cache, void*
     if (!aligned(key, 16) || !aligned(value, 16) || !aligned(key_cache, 16) || !aligned(value_cache, 16) ||
         !aligned(slot_mapping, 8))
         return set_error(PKV_ERR_INVALID, "%s: misaligned pointer", fn);
+    pkv::DebugChecks dbg((hipStream_t)stream, pkv::debug_checks_requested());
+    (void)dbg.slots(slot_mapping, num_tokens, block_size, num_blocks);
+    if (dbg.error() != hipSuccess) return hip_fail(dbg.error(), fn);
     pkv::CacheParams p;
+    p.guard = dbg.guard();
     p.key = key;
     p.value = value;
     p.kc = key_cache;
@@ -469,7 +523,7 @@ int reshape_and_cache(const void* key, const void* value, void* key_cache, void*
     p.BS = block_size;
     hipError_t e = pkv::launch_reshape_and_cache(p, dtype, (hipStream_t)stream);
     if (e != hipSuccess) return hip_fail(e, fn);
-    return PKV_OK;
+    return finish_checked(fn, dbg);
 }
 
 int copy_blocks(void* const* key_caches, void* const* value_caches, int num_layers, const int64_t* block_mapping,
@@ -490,7 +544,11 @@ int copy_blocks(void* const* key_caches, void* const* value_caches, int num_laye
             return set_error(PKV_ERR_INVALID, "%s: misaligned cache pointer for layer %d", fn, l);
     }
     const int esz = dtype == PKV_F32 ? 4 : 2;
+    pkv::DebugChecks dbg((hipStream_t)stream, pkv::debug_checks_requested());
+    (void)dbg.copies(block_mapping, num_pairs, num_blocks);
+    if (dbg.error() != hipSuccess) return hip_fail(dbg.error(), fn);
     pkv::CopyParams p;
+    p.guard = dbg.guard();
     p.mapping = block_mapping;
     p.num_pairs = num_pairs;
     p.block_bytes = (size_t)num_kv_heads * block_size * head_dim * esz;
@@ -503,7 +561,7 @@ int copy_blocks(void* const* key_caches, void* const* value_caches, int num_laye
         hipError_t e = pkv::launch_copy_blocks(p, nl, (hipStream_t)stream);
         if (e != hipSuccess) return hip_fail(e, fn);
     }
-    return PKV_OK;
+    return finish_checked(fn, dbg);
 }
 
 int pkv_read_probe(const void* buf, size_t bytes, void* sink, void* stream) {

@@ -35,6 +35,7 @@ __global__ __launch_bounds__(kCacheThreads) void reshape_and_cache_kernel(CacheP
     constexpr int VE = 16 / EB;                            // elements per 16-byte piece
     constexpr int kMaxRow = 128 * EB + 16;                 // LDS bytes per token row (D <= 128), padded
     __shared__ __attribute__((aligned(16))) char vrow[kTokGroup * kMaxRow];
+    if (contract_broken(p.guard)) return;
     const int g = blockIdx.x;
     const int h = blockIdx.y;
     const int i0 = g * kTokGroup;
@@ -86,6 +87,7 @@ constexpr int kCopySplit = 8;
 constexpr int kCopyUnroll = 4;
 
 __global__ __launch_bounds__(256) void copy_blocks_kernel(CopyParams p) {
+    if (contract_broken(p.guard)) return;
     const int piece = blockIdx.x % kCopySplit;
     const int pair = blockIdx.x / kCopySplit;
     const int layer = blockIdx.y;

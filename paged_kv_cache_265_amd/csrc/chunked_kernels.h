@@ -315,6 +315,7 @@ __device__ __forceinline__ void chunked_tile(const ChunkedParams& p, int idx, ch
 template <int K, int D, int BS>
 __global__ __launch_bounds__(NW * 64, 2) void chunked_fa(ChunkedParams p) {
     __shared__ __attribute__((aligned(16))) char lds[2 * ChunkLds<D>::STAGE];
+    if (contract_broken(p.guard)) return;
     chunked_tile<K, D, BS>(p, blockIdx.x, lds, false);
 }
 

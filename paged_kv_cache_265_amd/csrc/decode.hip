@@ -5,21 +5,21 @@
 
 namespace pkv {
 
-hipError_t launch_decode_bs16(const DecodeParams& p, int kind, int path, hipStream_t st) {
-    return launch_decode_block_size<16>(p, kind, path, st);
+hipError_t launch_decode_bs16(const DecodeParams& p, int kind, int path, int ring, hipStream_t st) {
+    return launch_decode_block_size<16>(p, kind, path, ring, st);
 }
 
-hipError_t launch_decode_path(const DecodeParams& p, int kind, int path, hipStream_t st) {
+hipError_t launch_decode_path(const DecodeParams& p, int kind, int path, int ring, hipStream_t st) {
     switch (p.BS) {
-    case 8: return launch_decode_bs8(p, kind, path, st);
-    case 16: return launch_decode_bs16(p, kind, path, st);
-    case 32: return launch_decode_bs32(p, kind, path, st);
+    case 8: return launch_decode_bs8(p, kind, path, ring, st);
+    case 16: return launch_decode_bs16(p, kind, path, ring, st);
+    case 32: return launch_decode_bs32(p, kind, path, ring, st);
     default: return hipErrorInvalidValue;
     }
 }
 
 hipError_t launch_decode(const DecodeParams& p, int kind, hipStream_t st) {
-    return launch_decode_path(p, kind, 0, st);
+    return launch_decode_path(p, kind, 0, 0, st);
 }
 
 int device_compute_units() {
@@ -33,8 +33,9 @@ int device_compute_units() {
     return v;
 }
 
-int split_waves_per_simd(int kind, int G, int D, int path) {
+int split_waves_per_simd(int kind, int G, int D, int path, int ring) {
     const bool mfma = kind != KF32 && (path == 2 || (path == 0 && G >= 4));
+    if (ring == 2) return 4;
     switch (kind * 1000 + D) {
     case KF32 * 1000 + 64: return per_simd_of<KF32, 64>(G, false);
     case KF32 * 1000 + 128: return per_simd_of<KF32, 128>(G, false);

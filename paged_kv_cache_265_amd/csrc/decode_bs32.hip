@@ -3,8 +3,8 @@
 
 namespace pkv {
 
-hipError_t launch_decode_bs32(const DecodeParams& p, int kind, int path, hipStream_t st) {
-    return launch_decode_block_size<32>(p, kind, path, st);
+hipError_t launch_decode_bs32(const DecodeParams& p, int kind, int path, int ring, hipStream_t st) {
+    return launch_decode_block_size<32>(p, kind, path, ring, st);
 }
 
 }  // namespace pkv

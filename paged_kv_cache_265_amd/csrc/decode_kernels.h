@@ -303,6 +303,7 @@ __device__ __forceinline__ void decode_split_wave(const DecodeParams& p, long lo
 
 template <class Loop, int R>
 __global__ __launch_bounds__(64, Loop::kWaves) void decode_split(DecodeParams p) {
+    if (contract_broken(p.guard)) return;
     decode_split_wave<Loop, R>(p, blockIdx.x, gridDim.x);
 }
 
@@ -311,6 +312,7 @@ __global__ __launch_bounds__(64, Loop::kWaves) void decode_split(DecodeParams p)
 // ---------------------------------------------------------------------------------------
 template <class Loop>
 __global__ __launch_bounds__(64, Loop::kWaves) void decode_fixed(DecodeParams p) {
+    if (contract_broken(p.guard)) return;
     constexpr int HT = Loop::HT;
     const int NS = p.Hkv * p.chunks;
     int idx = blockIdx.x;
@@ -368,6 +370,7 @@ __global__ __launch_bounds__(64, Loop::kWaves) void decode_fixed(DecodeParams p)
 // ---------------------------------------------------------------------------------------
 template <int K, int HT>
 __global__ __launch_bounds__(256) void decode_merge_stream(DecodeParams p, int split_waves) {
+    if (contract_broken(p.guard)) return;
     // the note, through scalar loads (fields: a, U as int64, then s, c, nb)
     const int32_t* nt = (const int32_t*)(p.notes + blockIdx.x);
     const int ns = scalar_load(nt, 4);
@@ -448,6 +451,7 @@ template <int K, int HT, int NG>
 __global__ __launch_bounds__(NG * 128) void decode_merge_head(DecodeParams p, int split_waves) {
     constexpr int kChunk = 16;  // pieces per group in flight at once
     __shared__ float other[NG - 1][128 + 2];
+    if (contract_broken(p.guard)) return;
     const int NS = p.Hkv * p.chunks;
     const int cap = min(p.G, HT);
     int idx = blockIdx.x;
@@ -556,6 +560,7 @@ __global__ __launch_bounds__(256) void decode_merge_fixed(DecodeParams p) {
     __shared__ float wts[kRound];
     __shared__ float red[8];
     __shared__ float part_o[128];
+    if (contract_broken(p.guard)) return;
     const int NS = p.Hkv * p.chunks;
     const int cap = min(p.G, HT);
     int idx = blockIdx.x;
@@ -632,12 +637,6 @@ inline int resident_waves(const void* f, int slot, int per_simd) {
 // the waves per SIMD the balanced split allows a loop (see run below)
 template <class Loop> constexpr int split_per_simd() { return Loop::kWaves == 1 ? 1 : 4; }
 
-// PKV_SPLIT_DEPTH=2 runs the balanced split with a two-tile ring (one block in
-// flight) instead of the inner loop's own depth; both pipelines stay tested
-inline bool shallow_split() {
-    const char* e = std::getenv("PKV_SPLIT_DEPTH");
-    return e && e[0] == '2' && e[1] == 0;
-}
 
 // merge of the balanced split's pieces (see merge_choice)
 template <int K, int HT>
@@ -651,14 +650,17 @@ void launch_split_merge(const DecodeParams& p, int NS, int cap, int waves, hipSt
     }
 }
 
+// shallow: the balanced split with a two-tile ring (one block in flight) instead of
+// the inner loop's own depth (a test and measurement variant; both pipelines stay
+// tested)
 template <class Loop, int K>
-hipError_t run(const DecodeParams& p0, bool split, int slot, hipStream_t st) {
+hipError_t run(const DecodeParams& p0, bool split, bool shallow, int slot, hipStream_t st) {
     DecodeParams p = p0;
     p.chunks = (p.G + Loop::HT - 1) / Loop::HT;
     const int NS = p.Hkv * p.chunks;
     int waves = 0;
     if (split) {
-        if (!shallow_split()) {
+        if (!shallow) {
             // deep-ring loops are built for one wave per SIMD; the others take what fits
             waves = resident_waves((const void*)decode_split<Loop, Loop::kRing>, slot * 2 + 1,
                                    split_per_simd<Loop>());
@@ -685,24 +687,23 @@ hipError_t run(const DecodeParams& p0, bool split, int slot, hipStream_t st) {
 }
 
 template <int K, int D, int BS>
-hipError_t dispatch(const DecodeParams& p, bool mfma, bool split, hipStream_t st) {
+hipError_t dispatch(const DecodeParams& p, bool mfma, bool split, bool shallow, hipStream_t st) {
     const int base = (K * 2 + (D == 128)) * 5;
     if constexpr (K != KF32) {
         if (mfma) {
-            if (p.G <= 16) return run<MfmaLoop<K, D, 1, BS>, K>(p, split, base + 0, st);
-            return run<MfmaWideLoop<K, D, BS>, K>(p, split, base + 1, st);
+            if (p.G <= 16) return run<MfmaLoop<K, D, 1, BS>, K>(p, split, shallow, base + 0, st);
+            return run<MfmaWideLoop<K, D, BS>, K>(p, split, shallow, base + 1, st);
         }
     }
-    if (p.G == 1) return run<ValuLoop<K, D, 1, BS>, K>(p, split, base + 2, st);
-    if (p.G == 2) return run<ValuLoop<K, D, 2, BS>, K>(p, split, base + 3, st);
-    return run<ValuLoop<K, D, 4, BS>, K>(p, split, base + 4, st);
+    if (p.G == 1) return run<ValuLoop<K, D, 1, BS>, K>(p, split, shallow, base + 2, st);
+    if (p.G == 2) return run<ValuLoop<K, D, 2, BS>, K>(p, split, shallow, base + 3, st);
+    return run<ValuLoop<K, D, 4, BS>, K>(p, split, shallow, base + 4, st);
 }
 
 // waves per SIMD of the balanced split for the loop dispatch() picks (block size
 // does not change it)
 template <int K, int D>
 int per_simd_of(int G, bool mfma) {
-    if (shallow_split()) return 4;
     if constexpr (K != KF32) {
         if (mfma) return G <= 16 ? split_per_simd<MfmaLoop<K, D, 1, 16>>() : split_per_simd<MfmaWideLoop<K, D, 16>>();
     }
@@ -711,18 +712,20 @@ int per_simd_of(int G, bool mfma) {
     return split_per_simd<ValuLoop<K, D, 4, 16>>();
 }
 
-// path: 0 automatic, 1 vector ALU inner loop, 2 matrix-core inner loop (16-bit types)
+// path: 0 automatic, 1 vector ALU inner loop, 2 matrix-core inner loop (16-bit types);
+// ring: 0 the loop's own prefetch depth, 2 a two-tile ring (balanced split only)
 template <int BS>
-hipError_t launch_decode_block_size(const DecodeParams& p, int kind, int path, hipStream_t st) {
+hipError_t launch_decode_block_size(const DecodeParams& p, int kind, int path, int ring, hipStream_t st) {
     const bool mfma = kind != KF32 && (path == 2 || (path == 0 && p.G >= 4));
     const bool split = p.part_tokens == 0;
+    const bool sh = ring == 2;
     switch (kind * 1000 + p.D) {
-    case KF32 * 1000 + 64: return dispatch<KF32, 64, BS>(p, false, split, st);
-    case KF32 * 1000 + 128: return dispatch<KF32, 128, BS>(p, false, split, st);
-    case KF16 * 1000 + 64: return dispatch<KF16, 64, BS>(p, mfma, split, st);
-    case KF16 * 1000 + 128: return dispatch<KF16, 128, BS>(p, mfma, split, st);
-    case KBF16 * 1000 + 64: return dispatch<KBF16, 64, BS>(p, mfma, split, st);
-    case KBF16 * 1000 + 128: return dispatch<KBF16, 128, BS>(p, mfma, split, st);
+    case KF32 * 1000 + 64: return dispatch<KF32, 64, BS>(p, false, split, sh, st);
+    case KF32 * 1000 + 128: return dispatch<KF32, 128, BS>(p, false, split, sh, st);
+    case KF16 * 1000 + 64: return dispatch<KF16, 64, BS>(p, mfma, split, sh, st);
+    case KF16 * 1000 + 128: return dispatch<KF16, 128, BS>(p, mfma, split, sh, st);
+    case KBF16 * 1000 + 64: return dispatch<KBF16, 64, BS>(p, mfma, split, sh, st);
+    case KBF16 * 1000 + 128: return dispatch<KBF16, 128, BS>(p, mfma, split, sh, st);
     default: return hipErrorInvalidValue;
     }
 }

@@ -177,6 +177,12 @@ __device__ __forceinline__ void mfma_result_fence() {
 
 // ---- misc ------------------------------------------------------------------------------
 
+// True when the call's contract pre-pass found a violation (see Guard): the kernel
+// then does nothing.  A NULL guard (checks off) costs one test of a kernel argument.
+__device__ __forceinline__ bool contract_broken(const unsigned long long* guard) {
+    return guard && *(const volatile unsigned long long*)guard != ~0ull;
+}
+
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
 __device__ __forceinline__ int lane_id() { return (int)(threadIdx.x & 63); }

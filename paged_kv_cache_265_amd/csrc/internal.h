@@ -6,6 +6,8 @@
 #include <stddef.h>
 #include <stdint.h>
 
+#include <mutex>
+
 namespace pkv {
 
 // The attention kernels work in tiles of 16 tokens of one kv head.  A KV block of
@@ -27,7 +29,13 @@ struct MergeNote {
 static_assert(sizeof(MergeNote) == 32 && offsetof(MergeNote, s) == 16 && offsetof(MergeNote, nb) == 24,
               "the merge reads the note as eight 32-bit words");
 
+// Every kernel takes `guard`: NULL, or the verdict word of the contract pre-pass
+// (PKV_DEBUG_CHECKS=1), which the kernel reads first and returns at once when it
+// holds a violation.
+typedef const unsigned long long* Guard;
+
 struct DecodeParams {
+    Guard guard;
     void* out;
     const void* q;
     const void* kc;
@@ -57,11 +65,12 @@ constexpr int kSimdsPerCu = 4;
 // compute units of the current device (cached per device; 256 when unknown)
 int device_compute_units();
 // waves per SIMD that the balanced split of paged_attention_decode launches at most
-// for this element kind, heads per kv head, head_dim and inner-loop choice (path:
-// 0 automatic, 1 vector ALU, 2 matrix cores)
-int split_waves_per_simd(int kind, int G, int D, int path);
+// for this element kind, heads per kv head, head_dim, inner-loop choice and ring
+// (as for launch_decode_path)
+int split_waves_per_simd(int kind, int G, int D, int path, int ring);
 
 struct ChunkedParams {
+    Guard guard;
     void* out;
     const void* q;
     const int32_t* cu_q_lens;
@@ -77,6 +86,7 @@ struct ChunkedParams {
 };
 
 struct CacheParams {
+    Guard guard;
     const void* key;
     const void* value;
     void* kc;
@@ -87,6 +97,7 @@ struct CacheParams {
 
 constexpr int kMaxLayersPerLaunch = 32;
 struct CopyParams {
+    Guard guard;
     void* k[kMaxLayersPerLaunch];
     void* v[kMaxLayersPerLaunch];
     const int64_t* mapping;
@@ -96,12 +107,13 @@ struct CopyParams {
 
 // kind: 0 f32, 1 f16, 2 bf16
 hipError_t launch_decode(const DecodeParams& p, int kind, hipStream_t stream);
-// path: 0 automatic, 1 vector ALU inner loop, 2 matrix-core inner loop (16-bit types)
-hipError_t launch_decode_path(const DecodeParams& p, int kind, int path, hipStream_t stream);
+// path: 0 automatic, 1 vector ALU inner loop, 2 matrix-core inner loop (16-bit types);
+// ring: 0 the inner loop's own prefetch depth, 2 a two-tile ring (balanced split)
+hipError_t launch_decode_path(const DecodeParams& p, int kind, int path, int ring, hipStream_t stream);
 // the same for one block size (one translation unit each)
-hipError_t launch_decode_bs8(const DecodeParams& p, int kind, int path, hipStream_t stream);
-hipError_t launch_decode_bs16(const DecodeParams& p, int kind, int path, hipStream_t stream);
-hipError_t launch_decode_bs32(const DecodeParams& p, int kind, int path, hipStream_t stream);
+hipError_t launch_decode_bs8(const DecodeParams& p, int kind, int path, int ring, hipStream_t stream);
+hipError_t launch_decode_bs16(const DecodeParams& p, int kind, int path, int ring, hipStream_t stream);
+hipError_t launch_decode_bs32(const DecodeParams& p, int kind, int path, int ring, hipStream_t stream);
 hipError_t launch_chunked(const ChunkedParams& p, int kind, hipStream_t stream);
 // one launch for a flattened batch: the one-row segments of cp through the decode
 // split described by dp (dp.cu_q = cp.cu_q_lens), the others as chunked tiles
@@ -114,6 +126,33 @@ hipError_t launch_read_probe(const void* buf, size_t bytes, void* sink, hipStrea
 // and the address of the current device's copy (looked up once per device).
 constexpr size_t kStaticScratchBytes = (size_t)64 << 20;
 hipError_t static_scratch_address(void** ptr);
+
+// The contract pre-pass of one call (contract.hip).  Inactive unless `on`; when
+// active it holds a process-wide lock for its lifetime, clears the verdict word,
+// enqueues the checks, and finish() copies the verdict back and waits for the
+// stream.  error() is the first HIP failure, if any.
+bool debug_checks_requested();  // PKV_DEBUG_CHECKS=1 in the environment
+class DebugChecks {
+public:
+    DebugChecks(hipStream_t stream, bool on);
+    bool on() const { return on_; }
+    Guard guard() const { return on_ ? verdict_ : nullptr; }
+    hipError_t error() const { return error_; }
+    hipError_t tables(const int32_t* bt, const int32_t* cl, const int32_t* cu, int rows, int MB, int BS, int NB,
+                      int total_q, int max_q_len);
+    hipError_t slots(const int64_t* sm, int n, int BS, int NB);
+    hipError_t copies(const int64_t* mapping, int P, int NB);
+    hipError_t finish(uint64_t* verdict);
+
+private:
+    hipStream_t stream_;
+    bool on_;
+    std::unique_lock<std::mutex> lock_;
+    unsigned long long* verdict_ = nullptr;
+    hipError_t error_ = hipSuccess;
+};
+// text for a verdict word other than PKV_CONTRACT_OK
+void describe_violation(uint64_t v, char* buf, size_t n);
 
 // thread-local message of pkv_last_error(); returns code
 int set_error(int code, const char* fmt, ...);

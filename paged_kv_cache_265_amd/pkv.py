@@ -21,7 +21,12 @@ LIB_PATH = os.path.join(HERE, "libpkv.so")
 F32, F16, BF16 = 0, 1, 2
 DTYPE_CODE = {torch.float32: F32, torch.float16: F16, torch.bfloat16: BF16}
 
-OK, ERR_INVALID, ERR_UNSUPPORTED, ERR_WORKSPACE, ERR_HIP = 0, -1, -2, -3, -4
+OK, ERR_INVALID, ERR_UNSUPPORTED, ERR_WORKSPACE, ERR_HIP, ERR_CONTRACT = 0, -1, -2, -3, -4, -6
+
+# device-side contract (include/pkv.h): verdict words and violation codes
+CONTRACT_OK = (1 << 64) - 1
+(BAD_CONTEXT_LEN, BAD_BLOCK_ID, BAD_QUERY_LENS, BAD_SLOT, DUPLICATE_SLOT, BAD_COPY_BLOCK, DUPLICATE_COPY_DST,
+ COPY_DST_IS_SRC) = range(1, 9)
 
 # every function include/pkv.h declares
 SYMBOLS = (
@@ -30,12 +35,20 @@ SYMBOLS = (
     "pkv_decode_workspace_size",
     "paged_attention_decode",
     "paged_attention_decode_static",
+    "pkv_decode_variant",
+    "pkv_decode_variant_workspace_size",
     "paged_attention_chunked",
     "paged_attention_mixed",
     "pkv_mixed_workspace_size",
     "reshape_and_cache",
     "copy_blocks",
     "pkv_read_probe",
+    "pkv_check_tables",
+    "pkv_check_slots",
+    "pkv_check_copies",
+    "pkv_check_tables_host",
+    "pkv_check_slots_host",
+    "pkv_check_copies_host",
     "pkv_error_string",
     "pkv_last_error",
 )
@@ -69,6 +82,10 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.paged_attention_decode.restype = I
     lib.paged_attention_decode_static.argtypes = [P, P, P, P, P, P, I, I, I, I, I, I, I, F, I, I, P]
     lib.paged_attention_decode_static.restype = I
+    lib.pkv_decode_variant.argtypes = [P, P, P, P, P, P, I, I, I, I, I, I, I, F, I, I, P, Z, I, I, P]
+    lib.pkv_decode_variant.restype = I
+    lib.pkv_decode_variant_workspace_size.argtypes = [I] * 10
+    lib.pkv_decode_variant_workspace_size.restype = Z
     lib.paged_attention_chunked.argtypes = [P, P, P, I, I, I, P, P, P, P, I, I, I, I, I, I, F, I, P]
     lib.paged_attention_chunked.restype = I
     lib.paged_attention_mixed.argtypes = [P, P, P, I, I, I, P, P, P, P, I, I, I, I, I, I, F, I, P, Z, P]
@@ -81,6 +98,17 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.copy_blocks.restype = I
     lib.pkv_read_probe.argtypes = [P, Z, P, P]
     lib.pkv_read_probe.restype = I
+    U64 = ctypes.c_uint64
+    lib.pkv_check_tables.argtypes = [P, P, P, I, I, I, I, I, I, P, P]
+    lib.pkv_check_slots.argtypes = [P, I, I, I, P, P]
+    lib.pkv_check_copies.argtypes = [P, I, I, P, P]
+    for f in (lib.pkv_check_tables, lib.pkv_check_slots, lib.pkv_check_copies):
+        f.restype = I
+    lib.pkv_check_tables_host.argtypes = [P, P, P, I, I, I, I, I, I]
+    lib.pkv_check_slots_host.argtypes = [P, I, I, I]
+    lib.pkv_check_copies_host.argtypes = [P, I, I]
+    for f in (lib.pkv_check_tables_host, lib.pkv_check_slots_host, lib.pkv_check_copies_host):
+        f.restype = U64
     lib.pkv_error_string.argtypes = [I]
     lib.pkv_error_string.restype = ctypes.c_char_p
     lib.pkv_last_error.argtypes = []
@@ -136,10 +164,19 @@ def decode_partition_size(num_seqs, num_q_heads, num_kv_heads, head_dim, block_s
     return rc
 
 
+SIZE_INVALID = (1 << 64) - 1  # PKV_SIZE_INVALID
+
+
+def _size(n: int) -> int:
+    if n == SIZE_INVALID:
+        raise PkvError(ERR_INVALID, load_library().pkv_last_error().decode())
+    return int(n)
+
+
 def decode_workspace_size(num_seqs, num_q_heads, num_kv_heads, head_dim, block_size, max_blocks_per_seq,
                           partition_size: int = 0) -> int:
-    return int(load_library().pkv_decode_workspace_size(num_seqs, num_q_heads, num_kv_heads, head_dim, block_size,
-                                                        max_blocks_per_seq, partition_size))
+    return _size(load_library().pkv_decode_workspace_size(num_seqs, num_q_heads, num_kv_heads, head_dim, block_size,
+                                                          max_blocks_per_seq, partition_size))
 
 
 def paged_attention_decode(out: torch.Tensor, query: torch.Tensor, key_cache: torch.Tensor,
@@ -163,6 +200,32 @@ def paged_attention_decode(out: torch.Tensor, query: torch.Tensor, key_cache: to
     rc = load_library().paged_attention_decode(
         _ptr(out), _ptr(query), _ptr(key_cache), _ptr(value_cache), _ptr(block_tables), _ptr(context_lens), S, Hq,
         Hkv, D, BS, NB, MB, float(scale), dt, int(partition_size), _ptr(workspace), ws_bytes, _stream(stream))
+    _check(rc)
+    return out
+
+
+INNER_LOOP = {"auto": 0, "valu": 1, "mfma": 2}
+
+
+def decode_variant(out: torch.Tensor, query: torch.Tensor, key_cache: torch.Tensor, value_cache: torch.Tensor,
+                   block_tables: torch.Tensor, context_lens: torch.Tensor, scale: float, partition_size: int = 0,
+                   inner_loop: str = "auto", ring: int = 0, stream=None) -> torch.Tensor:
+    """Test and measurement hook (pkv_decode_variant): paged_attention_decode with the
+    inner loop ("auto", "valu" or "mfma") and the prefetch ring (0: the loop's own, 2:
+    two tiles) forced.  The workspace is allocated here."""
+    _contig(out, query, key_cache, value_cache, block_tables, context_lens)
+    S, Hq, D = query.shape
+    NB, Hkv, BS, _ = key_cache.shape
+    MB = block_tables.shape[1] if block_tables.dim() == 2 else 0
+    dt = _dtype(out, query, key_cache, value_cache)
+    lib = load_library()
+    loop = INNER_LOOP[inner_loop]
+    need = _size(lib.pkv_decode_variant_workspace_size(S, Hq, Hkv, D, BS, max(MB, 1), partition_size, dt, loop,
+                                                       ring))
+    ws = torch.empty(max(need, 1), dtype=torch.uint8, device=query.device)
+    rc = lib.pkv_decode_variant(_ptr(out), _ptr(query), _ptr(key_cache), _ptr(value_cache), _ptr(block_tables),
+                                _ptr(context_lens), S, Hq, Hkv, D, BS, NB, MB, float(scale), dt, int(partition_size),
+                                _ptr(ws), need, loop, int(ring), _stream(stream))
     _check(rc)
     return out
 
@@ -208,7 +271,7 @@ def paged_attention_chunked(out: torch.Tensor, query: torch.Tensor, cu_q_lens: t
 
 
 def mixed_workspace_size(num_segs, num_q_heads, num_kv_heads, head_dim, block_size) -> int:
-    return int(load_library().pkv_mixed_workspace_size(num_segs, num_q_heads, num_kv_heads, head_dim, block_size))
+    return _size(load_library().pkv_mixed_workspace_size(num_segs, num_q_heads, num_kv_heads, head_dim, block_size))
 
 
 def paged_attention_mixed(out: torch.Tensor, query: torch.Tensor, cu_q_lens: torch.Tensor, max_q_len: int,
@@ -271,3 +334,72 @@ def read_probe(buf: torch.Tensor, sink: torch.Tensor, stream=None) -> None:
     nbytes = buf.numel() * buf.element_size()
     rc = load_library().pkv_read_probe(_ptr(buf), nbytes, _ptr(sink), _stream(stream))
     _check(rc)
+
+
+# ---- the device-side contract --------------------------------------------------------
+
+def violation(index: int, sub: int, code: int) -> int:
+    """The verdict word of one violation: (index << 32) | (sub-index << 8) | code."""
+    return (index << 32) | (min(max(sub, 0), 0xFFFFFF) << 8) | code
+
+
+def unpack_verdict(v: int):
+    """(index, sub-index, code) of a verdict word other than CONTRACT_OK."""
+    return v >> 32, (v >> 8) & 0xFFFFFF, v & 0xFF
+
+
+def _verdict_call(fn, *args, stream=None) -> int:
+    out = ctypes.c_uint64(CONTRACT_OK)
+    _check(fn(*args, ctypes.byref(out), _stream(stream)))
+    return out.value
+
+
+def check_tables(block_tables: torch.Tensor, context_lens: torch.Tensor, block_size: int, num_blocks: int,
+                 cu_q_lens: Optional[torch.Tensor] = None, total_q: int = 0, max_q_len: int = 0, stream=None) -> int:
+    """Verdict of the contract pre-pass over device block tables / context lengths
+    (and query lengths when cu_q_lens is given)."""
+    _contig(block_tables, context_lens)
+    rows, MB = block_tables.shape
+    return _verdict_call(load_library().pkv_check_tables, _ptr(block_tables), _ptr(context_lens), _ptr(cu_q_lens),
+                         rows, MB, block_size, num_blocks, total_q, max_q_len, stream=stream)
+
+
+def check_slots(slot_mapping: torch.Tensor, block_size: int, num_blocks: int, stream=None) -> int:
+    _contig(slot_mapping)
+    return _verdict_call(load_library().pkv_check_slots, _ptr(slot_mapping), slot_mapping.shape[0], block_size,
+                         num_blocks, stream=stream)
+
+
+def check_copies(block_mapping: torch.Tensor, num_blocks: int, stream=None) -> int:
+    _contig(block_mapping)
+    return _verdict_call(load_library().pkv_check_copies, _ptr(block_mapping), block_mapping.shape[0], num_blocks,
+                         stream=stream)
+
+
+def _host(a, dtype):
+    import numpy as np
+    return np.ascontiguousarray(np.asarray(a, dtype=dtype))
+
+
+def check_tables_host(block_tables, context_lens, block_size: int, num_blocks: int, cu_q_lens=None, total_q: int = 0,
+                      max_q_len: int = 0) -> int:
+    """The same verdict from the same item checks run on the CPU over host arrays."""
+    import numpy as np
+    bt, cl = _host(block_tables, np.int32), _host(context_lens, np.int32)
+    cu = None if cu_q_lens is None else _host(cu_q_lens, np.int32)
+    rows, MB = bt.shape
+    return int(load_library().pkv_check_tables_host(bt.ctypes.data, cl.ctypes.data,
+                                                    None if cu is None else cu.ctypes.data, rows, MB, block_size,
+                                                    num_blocks, total_q, max_q_len))
+
+
+def check_slots_host(slot_mapping, block_size: int, num_blocks: int) -> int:
+    import numpy as np
+    sm = _host(slot_mapping, np.int64)
+    return int(load_library().pkv_check_slots_host(sm.ctypes.data, sm.shape[0], block_size, num_blocks))
+
+
+def check_copies_host(block_mapping, num_blocks: int) -> int:
+    import numpy as np
+    bm = _host(block_mapping, np.int64).reshape(-1, 2)
+    return int(load_library().pkv_check_copies_host(bm.ctypes.data, bm.shape[0], num_blocks))

@@ -174,11 +174,37 @@ def test_decode_empty_batch_is_a_no_op():
     assert _decode(num_seqs=0, out=None, query=None) == 0
 
 
-def test_decode_path_override_is_checked(monkeypatch):
-    monkeypatch.setenv("PKV_DECODE_PATH", "bogus")
-    assert _decode() == pkv.pkv.ERR_INVALID
-    monkeypatch.setenv("PKV_DECODE_PATH", "mfma")
-    assert _decode(dtype=0) == pkv.pkv.ERR_UNSUPPORTED
+def test_decode_variant_arguments_are_checked():
+    lib = pkv.load_library()
+    a = dict(out=FAKE, query=FAKE, key_cache=FAKE, value_cache=FAKE, block_tables=FAKE, context_lens=FAKE,
+             num_seqs=2, num_q_heads=8, num_kv_heads=2, head_dim=128, block_size=16, num_blocks=10,
+             max_blocks_per_seq=4, scale=0.1, dtype=2, partition_size=0, workspace=None, workspace_bytes=0)
+
+    def call(inner_loop, ring, **over):
+        b = dict(a, **over)
+        return lib.pkv_decode_variant(*b.values(), inner_loop, ring, None)
+
+    assert call(3, 0) == pkv.pkv.ERR_INVALID
+    assert call(-1, 0) == pkv.pkv.ERR_INVALID
+    assert call(0, 1) == pkv.pkv.ERR_INVALID
+    assert call(2, 0, dtype=0) == pkv.pkv.ERR_UNSUPPORTED  # no fp32 matrix-core loop
+    assert call(1, 2) == pkv.pkv.ERR_WORKSPACE             # valid, but no workspace given
+    # a two-tile ring takes up to four waves per SIMD, so up to four times the records
+    base = lib.pkv_decode_variant_workspace_size(2, 8, 2, 128, 16, 4, 0, 2, 0, 0)
+    assert base == pkv.decode_workspace_size(2, 8, 2, 128, 16, 4)
+    assert lib.pkv_decode_variant_workspace_size(2, 8, 2, 128, 16, 4, 0, 2, 0, 2) > 3 * base // 2
+
+
+def test_workspace_sizes_tell_invalid_from_none():
+    assert pkv.decode_workspace_size(0, 8, 2, 128, 16, 4) == 0            # nothing to decode
+    assert pkv.decode_workspace_size(8, 8, 8, 64, 16, 32, 512) == 0        # one partition fits all
+    for bad in [(-1, 8, 2, 128, 16, 4, 0), (2, 8, 3, 128, 16, 4, 0), (2, 8, 2, 128, 16, 0, 0),
+                (2, 8, 2, 128, 16, 4, 24), (2, 0, 1, 128, 16, 4, 0)]:
+        with pytest.raises(pkv.PkvError):
+            pkv.decode_workspace_size(*bad)
+    with pytest.raises(pkv.PkvError):
+        pkv.mixed_workspace_size(4, 7, 2, 128, 16)
+    assert pkv.mixed_workspace_size(0, 8, 2, 128, 16) == 0
 
 
 def _chunked(**over):

@@ -23,15 +23,18 @@ def say(msg):
     print(msg, flush=True)
 
 
-def decode_on(paged, case, partition_size=0):
+def decode_on(paged, case, partition_size=0, inner_loop=None):
     bs = paged.pool.block_size
     say(f"decode bs={bs} {case.dtype} S={case.num_seqs} Hq={case.num_q_heads} Hkv={case.num_kv_heads} "
-        f"D={case.head_dim} part={partition_size} ctx={paged.context_lens.tolist()}")
+        f"D={case.head_dim} part={partition_size} loop={inner_loop or 'auto'} ctx={paged.context_lens.tolist()}")
     q = dev(case.query)
     out = torch.full_like(q, float("nan"))
-    pkv.paged_attention_decode(out, q, dev(paged.pool.key_cache), dev(paged.pool.value_cache),
-                               dev(paged.block_tables), dev(paged.context_lens), case.scale,
-                               partition_size=partition_size)
+    args = (out, q, dev(paged.pool.key_cache), dev(paged.pool.value_cache), dev(paged.block_tables),
+            dev(paged.context_lens), case.scale)
+    if inner_loop is None:
+        pkv.paged_attention_decode(*args, partition_size=partition_size)
+    else:
+        pkv.decode_variant(*args, partition_size=partition_size, inner_loop=inner_loop)
     torch.cuda.synchronize()
     return out
 
@@ -73,11 +76,10 @@ def test_decode_block_size_matches_oracle_and_bs16(bs, dtype, G, Hkv, D, ctx):
 
 @pytest.mark.parametrize("bs", [8, 32])
 @pytest.mark.parametrize("path", ["valu", "mfma"])
-def test_decode_block_size_both_inner_loops(bs, path, monkeypatch):
-    monkeypatch.setenv("PKV_DECODE_PATH", path)
+def test_decode_block_size_both_inner_loops(bs, path):
     case = make_decode_case([63, bs], "bf16", [5, 300, 1025, 64], 8, 2, 128)
     p = reblock(case.paged, bs, np.random.default_rng(bs))
-    check_close(decode_on(p, case), oracle_on(p, case), "bf16", f"{path} bs={bs}")
+    check_close(decode_on(p, case, inner_loop=path), oracle_on(p, case), "bf16", f"{path} bs={bs}")
 
 
 @pytest.mark.parametrize("bs", [8, 32])

@@ -19,15 +19,22 @@ from helpers import bits, check_close, dev, oracle_decode_case
 pytestmark = pytest.mark.gpu
 
 
-def run_decode(case, partition_size=0, bt=None, kc=None, vc=None, query=None):
+def run_decode(case, partition_size=0, bt=None, kc=None, vc=None, query=None, inner_loop=None, ring=0):
+    """paged_attention_decode, or with inner_loop / ring given the test hook that forces
+    the inner loop ("valu" / "mfma") or a two-tile prefetch ring."""
     say(f"decode {case.label or ''} S={case.num_seqs} Hq={case.num_q_heads} Hkv={case.num_kv_heads} "
-        f"D={case.head_dim} {case.dtype} part={partition_size} max_ctx={int(case.context_lens.max(initial=0))}")
+        f"D={case.head_dim} {case.dtype} part={partition_size} max_ctx={int(case.context_lens.max(initial=0))} "
+        f"loop={inner_loop or 'auto'} ring={ring}")
     q = dev(case.query if query is None else query)
     kc = dev(case.pool.key_cache) if kc is None else kc
     vc = dev(case.pool.value_cache) if vc is None else vc
     out = torch.full_like(q, float("nan"))
-    pkv.paged_attention_decode(out, q, kc, vc, dev(case.block_tables if bt is None else bt),
-                               dev(case.context_lens), case.scale, partition_size=partition_size)
+    bt_d, cl_d = dev(case.block_tables if bt is None else bt), dev(case.context_lens)
+    if inner_loop is None and ring == 0:
+        pkv.paged_attention_decode(out, q, kc, vc, bt_d, cl_d, case.scale, partition_size=partition_size)
+    else:
+        pkv.decode_variant(out, q, kc, vc, bt_d, cl_d, case.scale, partition_size=partition_size,
+                           inner_loop=inner_loop or "auto", ring=ring)
     torch.cuda.synchronize()
     return out
 
@@ -67,11 +74,10 @@ def test_decode_matches_oracle(dtype, G, Hkv, D, ctx):
 
 @pytest.mark.parametrize("path", ["valu", "mfma"])
 @pytest.mark.parametrize("dtype,G", [("bf16", 4), ("f16", 1), ("bf16", 2), ("f16", 32)])
-def test_both_inner_loops_match_oracle(path, dtype, G, monkeypatch):
-    monkeypatch.setenv("PKV_DECODE_PATH", path)
+def test_both_inner_loops_match_oracle(path, dtype, G):
     Hkv = 2 if G < 32 else 1
     case = make_decode_case([22, G], dtype, [3, 700, 1025, 64], G * Hkv, Hkv, 128)
-    check_close(run_decode(case), oracle_decode_case(case), dtype, f"{path} {dtype} G={G}")
+    check_close(run_decode(case, inner_loop=path), oracle_decode_case(case), dtype, f"{path} {dtype} G={G}")
 
 
 @pytest.mark.parametrize("dtype,G", [("bf16", 4), ("f16", 1), ("f32", 2), ("bf16", 32)])
@@ -235,12 +241,11 @@ def test_streams_are_honoured():
     ("bf16", 40, 2, 64, [3000, 33]),            # heads per kv head above one 32-head chunk
     ("f32", 2, 2, 64, [7000, 0, 16]),
 ])
-def test_balanced_split_edges(depth, dtype, G, Hkv, D, ctx, monkeypatch):
+def test_balanced_split_edges(depth, dtype, G, Hkv, D, ctx):
     """The load-balanced schedule: streams split across many waves, empty streams,
     waves with no work, and both prefetch depths."""
-    monkeypatch.setenv("PKV_SPLIT_DEPTH", depth)
     case = make_decode_case([34, G, len(ctx)], dtype, ctx, G * Hkv, Hkv, D)
-    out = run_decode(case, partition_size=0)
+    out = run_decode(case, partition_size=0, ring=2 if depth == "2" else 0)
     check_close(out, oracle_decode_case(case), dtype, f"split depth {depth}")
     for s, n in enumerate(ctx):
         if n == 0:
