@@ -645,7 +645,8 @@ def run_cow(args, torch, pkv, workloads, dev):
 
 
 # (label, dtype, context lengths, query heads, kv heads): batches from one long sequence
-# to many short ones, whose split streams are merged in different ways
+# to many short ones, whose split streams are merged in different ways; ("uniform", n,
+# lo, hi) draws n lengths from U{lo..hi} (seeded)
 SHAPES = [
     ("GQA 32/8 bf16, 1 x 131072", "bf16", [131072], 32, 8),
     ("GQA 32/8 bf16, 2 x 65536", "bf16", [65536] * 2, 32, 8),
@@ -655,6 +656,10 @@ SHAPES = [
     ("MQA 32/1 bf16, 4 x 131072", "bf16", [131072] * 4, 32, 1),
     ("MQA 32/1 bf16, 256 x 4096", "bf16", [4096] * 256, 32, 1),
     ("MHA 40 f16, 1 x 65536", "f16", [65536], 40, 40),
+    ("GQA 32/8 bf16, 256 x U{64..512}", "bf16", ("uniform", 256, 64, 512), 32, 8),
+    ("GQA 32/8 bf16, 1024 x U{64..512}", "bf16", ("uniform", 1024, 64, 512), 32, 8),
+    ("GQA 32/8 bf16, 4096 x U{64..512}", "bf16", ("uniform", 4096, 64, 512), 32, 8),
+    ("GQA 32/8 bf16, 16384 x U{64..512}", "bf16", ("uniform", 16384, 64, 512), 32, 8),
 ]
 
 
@@ -664,7 +669,14 @@ def run_shapes(args, torch, pkv, workloads, dev):
     rounds of `steps` calls back to back per shape."""
     from workloads.gen import make_decode_case
     rows = []
+    import numpy as np
+    only = getattr(args, "shape_filter", None)
     for i, (label, dt, ctx, hq, hkv) in enumerate(SHAPES):
+        if only and only not in label:
+            continue
+        if isinstance(ctx, tuple):
+            _, n, lo, hi = ctx
+            ctx = np.random.default_rng([265, 91, i]).integers(lo, hi, size=n, endpoint=True)
         c = make_decode_case([265, 90, i], dt, ctx, hq, hkv, 128)
         kc, vc, q = c.pool.key_cache.to(dev), c.pool.value_cache.to(dev), c.query.to(dev)
         bt, cl = torch.from_numpy(c.block_tables).to(dev), torch.from_numpy(c.context_lens).to(dev)

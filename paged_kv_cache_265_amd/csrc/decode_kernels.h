@@ -76,16 +76,10 @@ __device__ __forceinline__ TileSrc tile_src(const DecodeParams& p, int s, int b,
     return t;
 }
 
-__device__ __forceinline__ int wave_sum_int(int v) {
-#pragma unroll
-    for (int m = 1; m < 64; m <<= 1) v += __shfl_xor(v, m, 64);
-    return v;
-}
-
-__device__ __forceinline__ int wave_incl_scan(int v, int lane) {
+__device__ __forceinline__ long long wave_incl_scan(long long v, int lane) {
 #pragma unroll
     for (int off = 1; off < 64; off <<= 1) {
-        const int y = __shfl_up(v, off, 64);
+        const long long y = __shfl_up(v, off, 64);
         if (lane >= off) v += y;
     }
     return v;
@@ -105,34 +99,78 @@ __device__ __forceinline__ Heads stream_heads(const DecodeParams& p, int c) {
     return h;
 }
 
-// Sum over all sequences of their tile counts, with every context length of a round
-// of 256 sequences loaded at once.  Wave w of N also writes the zero output of each
-// empty decode sequence s with s % N == w (16-byte stores of a whole output row).
+// ---------------------------------------------------------------------------------------
+// Where the balanced split's waves start.  Every wave needs the batch's unit count U
+// and the sequence holding its first unit; the merge needs starts[s] = NS * (tiles of
+// the decode sequences before s) for s = 0..S (starts[S] = U).
+//  * Batches of at most kInWaveSeqs sequences: every split wave loads all context
+//    lengths in one round (four per lane) and finds both from its registers; wave 0
+//    writes starts[].
+//  * Larger batches: a first launch of one workgroup (decode_split_prologue) scans the
+//    tile counts, kPrologueThreads sequences at a time, into starts[]; each split wave
+//    then reads U and finds its sequence with 64-way searches over starts[] (two
+//    rounds of one load per lane for up to 4096 sequences), so the start-up of a wave
+//    no longer grows with the batch.
+// Empty decode sequences get a zero output: from the prologue, or from split wave
+// s mod N in small batches (16-byte stores of a whole output row).
+// ---------------------------------------------------------------------------------------
+constexpr int kInWaveSeqs = 256;
+constexpr int kPrologueThreads = 1024;
+
 template <int EB>
-__device__ long long total_blocks(const DecodeParams& p, int lane, int w, int N) {
-    long long tot = 0;
-    for (int base = 0; base < p.S; base += 256) {
-        int nb[4];
-        bool empty[4];
+__global__ __launch_bounds__(kPrologueThreads) void decode_split_prologue(DecodeParams p, int NS) {
+    constexpr int kWaves = kPrologueThreads / 64;
+    __shared__ long long wave_tot[kWaves];
+    if (contract_broken(p.guard)) return;
+    const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+    long long carry = 0;
+    for (int base = 0; base < p.S; base += kPrologueThreads) {
+        const int s = base + tid;
+        const bool dec = s < p.S && is_decode(p, s);
+        const int nb = dec ? ntiles(p.context_lens[s]) : 0;
+        const long long incl = wave_incl_scan((long long)nb, lane);
+        if (lane == 63) wave_tot[wv] = incl;
+        __syncthreads();
+        long long before = carry, round = 0;
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            const int s = base + 64 * j + lane;
-            const bool dec = s < p.S && is_decode(p, s);
-            nb[j] = dec ? ntiles(p.context_lens[s]) : 0;
-            empty[j] = dec && nb[j] == 0 && s % N == w;
+        for (int k = 0; k < kWaves; ++k) {
+            const long long t = wave_tot[k];
+            before += k < wv ? t : 0;
+            round += t;
         }
-        tot += wave_sum_int(nb[0] + nb[1] + nb[2] + nb[3]);
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            for (unsigned long long e = __ballot(empty[j]); e; e &= e - 1) {
-                const int s = base + 64 * j + __builtin_ctzll(e);
-                const size_t n16 = (size_t)p.Hq * p.D * EB / 16;
-                uint4* row = (uint4*)((char*)p.out + row_of_uniform(p, s) * p.Hq * p.D * EB);
-                for (size_t i = lane; i < n16; i += 64) row[i] = make_uint4(0, 0, 0, 0);
-            }
+        if (s < p.S) p.starts[s] = (long long)NS * (before + incl - nb);
+        if (dec && nb == 0) {
+            const size_t n16 = (size_t)p.Hq * p.D * EB / 16;
+            uint4* row = (uint4*)((char*)p.out + row_of(p, s) * p.Hq * p.D * EB);
+            for (size_t i = 0; i < n16; ++i) row[i] = make_uint4(0, 0, 0, 0);
         }
+        carry += round;
+        __syncthreads();  // wave_tot is rewritten by the next round
     }
-    return tot;
+    if (tid == 0) p.starts[p.S] = (long long)NS * carry;
+}
+
+// The sequence s whose units [starts[s], starts[s+1]) contain unit u (0 <= u < U):
+// the last s with starts[s] <= u, found by 64-way searches (one load per lane each;
+// two rounds for up to 4096 sequences).
+__device__ __forceinline__ long long read_lane64(long long v, int src) {
+    const uint64_t lo = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)v, src);
+    const uint64_t hi = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)((uint64_t)v >> 32), src);
+    return (long long)(lo | (hi << 32));
+}
+
+__device__ __forceinline__ int sequence_of_unit(const long long* starts, int S, long long u, int lane) {
+    int a = 0, b = S;  // starts[a] <= u; the answer lies in [a, b)
+    while (b - a > 1) {
+        const int step = (b - a + 63) / 64;
+        const int idx = a + lane * step;
+        const unsigned long long le = __ballot(idx < b && starts[idx] <= u);
+        a += (63 - __builtin_clzll(le)) * step;  // lane 0 always qualifies (idx = a)
+        b = min(b, a + step);
+        a = uniform(a);
+        b = uniform(b);
+    }
+    return a;
 }
 
 // Which merge joins the pieces of the balanced split, from what the host knows (the
@@ -178,44 +216,76 @@ __device__ __forceinline__ void decode_split_wave(const DecodeParams& p, long lo
     constexpr int HT = Loop::HT;
     const int lane = lane_id();
     const int NS = p.Hkv * p.chunks;
-    // The unit count comes out of lane reductions and the range bounds out of 64-bit
-    // divisions, which run on the vector unit: all are asserted wave-uniform, so that
-    // the counts and cursors derived from them, and the branches on those, are scalar.
-    const long long U = uniform(total_blocks<Loop::kElemBytes>(p, lane, (int)w, (int)N_launched) * NS);
+    // small batches: sequence 64 j + lane's context and its first unit, in registers
+    const bool small = p.S <= kInWaveSeqs;
+    int ctxr[4];
+    long long first[4];
+    long long tiles = 0;
+    if (small) {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const int s = 64 * j + lane;
+            const bool dec = s < p.S && is_decode(p, s);
+            ctxr[j] = dec ? p.context_lens[s] : 0;
+            const int nb = ntiles(ctxr[j]);
+            const long long incl = wave_incl_scan((long long)nb, lane);
+            first[j] = (long long)NS * (tiles + incl - nb);
+            tiles += uniform(read_lane64(incl, 63));
+            for (unsigned long long e = __ballot(dec && nb == 0 && s % N_launched == w); e; e &= e - 1) {
+                const int se = 64 * j + __builtin_ctzll(e);
+                const size_t n16 = (size_t)p.Hq * p.D * Loop::kElemBytes / 16;
+                uint4* row = (uint4*)((char*)p.out + row_of_uniform(p, se) * p.Hq * p.D * Loop::kElemBytes);
+                for (size_t i = lane; i < n16; i += 64) row[i] = make_uint4(0, 0, 0, 0);
+            }
+        }
+        if (w == 0) {
+#pragma unroll
+            for (int j = 0; j < 4; ++j)
+                if (64 * j + lane < p.S) p.starts[64 * j + lane] = first[j];
+            if (lane == 0) p.starts[p.S] = (long long)NS * tiles;
+        }
+    }
+    // The unit count and the range bounds (64-bit divisions, which run on the vector
+    // unit) are asserted wave-uniform, so that the counts and cursors derived from
+    // them, and the branches on those, are scalar.
+    const long long U = uniform(small ? (long long)NS * tiles : p.starts[p.S]);
     const long long N = uniform(working_waves(U, N_launched));
     const long long lo = w < N ? uniform(w * U / N) : U, hi = w < N ? uniform((w + 1) * U / N) : U;
-    // starts[s] = unit of sequence s's first block (written by the wave that folds
-    // it), starts[S] = U: the merge finds every stream's pieces from these
-    if (w == 0 && lane == 0) p.starts[p.S] = U;
     if (lo >= hi) {
         if (lane == 0) p.notes[w] = MergeNote{0, U, -1, 0, 0, 0};
         return;
     }
 
-    // locate unit lo: sequence s whose units [NS*cum(s), NS*cum(s+1)) contain it
+    // locate unit lo: its sequence, then its stream and tile inside the sequence
     struct Cursor {
         int s, c, b, nb, ctx;
     } cur;
     {
-        long long run = 0;
-        for (int base = 0;; base += 64) {
-            const int s = base + lane;
-            const int ctx = s < p.S ? dec_ctx(p, s) : 0;
-            const int nb = ntiles(ctx);
-            const int incl = wave_incl_scan(nb, lane);
-            const unsigned long long hit = __ballot(run + (long long)NS * incl > lo);
-            if (hit) {
-                const int t = __builtin_ctzll(hit);
-                cur.s = base + t;
-                cur.nb = read_lane(nb, t);
-                cur.ctx = read_lane(ctx, t);
-                const long long r = lo - (run + (long long)NS * (read_lane(incl, t) - cur.nb));
-                cur.c = (int)(r / cur.nb);
-                cur.b = (int)(r - (long long)cur.c * cur.nb);
-                break;
+        long long a0 = 0;  // first unit of sequence cur.s
+        if (small) {
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const long long units = (long long)NS * ntiles(ctxr[j]);
+                const unsigned long long h = __ballot(first[j] <= lo && lo < first[j] + units);
+                if (h) {
+                    const int t = __builtin_ctzll(h);
+                    cur.s = 64 * j + t;
+                    cur.ctx = read_lane(ctxr[j], t);
+                    a0 = read_lane64(first[j], t);
+                    break;
+                }
             }
-            run += (long long)NS * read_lane(incl, 63);
+        } else {
+            cur.s = sequence_of_unit(p.starts, p.S, lo, lane);
+            cur.ctx = dec_ctx_uniform(p, cur.s);
+            a0 = p.starts[cur.s];
         }
+        cur.s = uniform(cur.s);
+        cur.ctx = uniform(cur.ctx);
+        cur.nb = ntiles(cur.ctx);
+        const long long r = lo - uniform(a0);
+        cur.c = (int)(r / cur.nb);
+        cur.b = (int)(r - (long long)cur.c * cur.nb);
     }
     // merge note: this wave merges the stream it starts in when that stream began in
     // an earlier wave and ends in this one
@@ -259,7 +329,6 @@ __device__ __forceinline__ void decode_split_wave(const DecodeParams& p, long lo
         }
     };
     auto compute = [&](typename Loop::Tile& t) {
-        if (cc.b == 0 && cc.c == 0 && lane == 0) p.starts[cc.s] = lo + done;
         L.block(st, t, cc.ctx - cc.b * kTileTokens, p.scale_log2);
         if (done + 1 == cnt || cc.b + 1 == cc.nb) {
             L.finish(st);
@@ -660,6 +729,9 @@ hipError_t run(const DecodeParams& p0, bool split, bool shallow, int slot, hipSt
     const int NS = p.Hkv * p.chunks;
     int waves = 0;
     if (split) {
+        if (p.S > kInWaveSeqs)
+            hipLaunchKernelGGL((decode_split_prologue<Loop::kElemBytes>), dim3(1), dim3(kPrologueThreads), 0, st, p,
+                               NS);
         if (!shallow) {
             // deep-ring loops are built for one wave per SIMD; the others take what fits
             waves = resident_waves((const void*)decode_split<Loop, Loop::kRing>, slot * 2 + 1,

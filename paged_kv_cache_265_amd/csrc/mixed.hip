@@ -49,6 +49,8 @@ hipError_t go(const DecodeParams& dp0, const ChunkedParams& cp, hipStream_t st) 
     if (decode_wgs * NW > kMaxSplitWaves) decode_wgs = kMaxSplitWaves / NW;
     const long long tiles = ((long long)cp.max_q_len * cp.G + ROWS_PER_WG - 1) / ROWS_PER_WG;
     const long long grid = decode_wgs + tiles * cp.Hkv * cp.num_segs;
+    if (dp.S > kInWaveSeqs)
+        hipLaunchKernelGGL((decode_split_prologue<Loop::kElemBytes>), dim3(1), dim3(kPrologueThreads), 0, st, dp, NS);
     hipLaunchKernelGGL((mixed_kernel<Loop, K, D, BS>), dim3((unsigned)grid), dim3(NW * 64), 0, st, dp, cp,
                        decode_wgs);
     hipError_t e = hipGetLastError();

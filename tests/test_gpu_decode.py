@@ -240,6 +240,10 @@ def test_streams_are_honoured():
     ("bf16", 32, 1, 128, [20000, 17, 4096]),
     ("bf16", 40, 2, 64, [3000, 33]),            # heads per kv head above one 32-head chunk
     ("f32", 2, 2, 64, [7000, 0, 16]),
+    # more sequences than one round of in-wave loads: the start units come from the
+    # prologue's scan (three rounds of 1024 sequences), empty contexts among them
+    ("bf16", 4, 2, 128, [0 if i % 11 == 3 else 1 + (i * 37) % 200 for i in range(3000)]),
+    ("f16", 1, 2, 64, [0] * 300 + [17]),
 ])
 def test_balanced_split_edges(depth, dtype, G, Hkv, D, ctx):
     """The load-balanced schedule: streams split across many waves, empty streams,

@@ -77,6 +77,9 @@ CASES = [
     ("bf16", 20, 2, 128, [1, 900, 60], [1, 1, 9]),
     ("bf16", 4, 8, 128, [5000, 3000, 1, 800, 50], [1, 1, 1, 1, 1]),      # decode only
     ("f16", 4, 2, 128, [0, 100], [50, 7]),                                 # prefill only
+    # more segments than one round of in-wave loads: the decode start units come from
+    # the prologue's scan
+    ("bf16", 8, 1, 128, [40 + (i * 53) % 900 for i in range(300)] + [700, 0], [1] * 300 + [33, 64]),
 ]
 
 
