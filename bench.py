@@ -31,6 +31,7 @@ sys.path.insert(0, ROOT)
 
 METRIC = "paged-attn decode achieved HBM GB/s (% of MI355X peak) + sequences/sec"
 PEAK_HBM_GBS = 8000.0
+PEAK_MFMA_TFLOPS = 2500.0  # dense bf16 / f16 matrix-core peak of MI355X
 PROFILES = os.path.join(ROOT, "profiles")
 # sources of the decode kernels: counter summaries are valid only for these exact files
 KERNEL_SOURCES = [os.path.join(ROOT, "paged_kv_cache_265_amd", "csrc", f)
@@ -231,7 +232,8 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
-    ap.add_argument("--workload", default="gqa", choices=["gqa", "opt13b", "tiny", "long", "cow", "beam", "shapes"])
+    ap.add_argument("--workload", default="gqa", choices=["gqa", "opt13b", "tiny", "long", "cow", "beam", "shapes",
+                                                             "prefill"])
     ap.add_argument("--partition-size", type=int, default=None)
     ap.add_argument("--paging-study", action="store_true",
                     help="time the decode call on the same batch with shuffled and with contiguous block "
@@ -277,6 +279,8 @@ def main():
         return run_beam(args, torch, pkv, workloads, dev)
     if args.workload == "shapes":
         return run_shapes(args, torch, pkv, workloads, dev)
+    if args.workload == "prefill":
+        return run_prefill(args, torch, pkv, workloads, dev)
     W = build_workload(args.workload)
     case = W["decode"]
     part = W["partition_size"] if args.partition_size is None else args.partition_size
@@ -704,6 +708,55 @@ def run_shapes(args, torch, pkv, workloads, dev):
         torch.cuda.empty_cache()
     print(json.dumps({"metric": METRIC, "workload": "decode call over batch shapes", "unit": "GB/s",
                       "steps": args.steps, "warmup": args.warmup, "shapes": rows}), flush=True)
+
+
+# (label, dtype, query heads, kv heads): the chunked-prefill shapes timed by
+# --workload prefill, each 8 segments of 512 query rows over 4096 cached tokens
+PREFILL = [
+    ("MQA 32/1 bf16", "bf16", 32, 1),
+    ("GQA 32/8 bf16", "bf16", 32, 8),
+    ("MHA 32 f16", "f16", 32, 32),
+]
+
+
+def run_prefill(args, torch, pkv, workloads, dev):
+    """The chunked-prefill call alone on the long mixed workload's prefill shape (8
+    segments of 512 query rows over 4096 cached tokens plus the chunk, head_dim 128;
+    seeded N(0,1), shuffled placement; the chunks written by reshape_and_cache first)
+    for three head layouts: the best of three rounds of `steps` calls back to back.
+    Lighter than --workload long (no long decode pool), for profiling the kernel."""
+    from workloads.gen import make_chunked_case
+    rows = []
+    for i, (label, dt, hq, hkv) in enumerate(PREFILL):
+        c = make_chunked_case([265, 95, i], dt, [4096] * 8, [512] * 8, hq, hkv, 128)
+        p = c.paged
+        kc, vc = p.pool.key_cache.to(dev), p.pool.value_cache.to(dev)
+        pkv.reshape_and_cache(c.new_key.to(dev), c.new_value.to(dev), kc, vc, torch.from_numpy(c.slot_mapping).to(dev))
+        q, cu = c.query.to(dev), torch.from_numpy(c.cu_q_lens).to(dev)
+        bt, cl = torch.from_numpy(p.block_tables).to(dev), torch.from_numpy(p.context_lens).to(dev)
+        out = torch.empty_like(q)
+        flops = workloads.algorithmic_chunked_flops(p.context_lens, np.diff(c.cu_q_lens), hq, 128)
+        best = None
+        for _ in range(3):
+            for _ in range(args.warmup):
+                pkv.paged_attention_chunked(out, q, cu, 512, kc, vc, bt, cl, c.scale)
+            torch.cuda.synchronize()
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            for _ in range(args.steps):
+                pkv.paged_attention_chunked(out, q, cu, 512, kc, vc, bt, cl, c.scale)
+            e1.record()
+            torch.cuda.synchronize()
+            ms = e0.elapsed_time(e1) / args.steps
+            best = ms if best is None else min(best, ms)
+        tf = flops / (best * 1e-3) / 1e12
+        rows.append({"shape": label, "call_us": round(best * 1e3, 1), "flops": flops, "TFLOPs": round(tf, 1),
+                     "frac_of_bf16_f16_mfma_peak": round(tf / PEAK_MFMA_TFLOPS, 4)})
+        log(f"{label}: {best * 1e3:.1f} us, {tf:.0f} TFLOP/s")
+        del kc, vc, q, out, c, p
+        torch.cuda.empty_cache()
+    print(json.dumps({"metric": METRIC, "workload": "chunked-prefill call, 8 x 512 rows over 4608 keys",
+                      "unit": "TFLOP/s", "steps": args.steps, "warmup": args.warmup, "shapes": rows}), flush=True)
 
 
 def run_beam(args, torch, pkv, workloads, dev):

@@ -11,17 +11,26 @@
 // the heads sharing one kv head share every K/V tile.  A workgroup of 4 waves takes
 // 128 consecutive rows of one (segment, kv head); each wave owns 32 of them (two
 // 16-row matrix-core columns), so every K/V operand read from LDS serves 32 rows.
-// The keys go by in steps of 32 (two pool blocks of 16 tokens, one of 32, or four of
-// 8): the workgroup stages a step's K and V into LDS once, double-buffered, and every
-// wave folds it into its rows with an online softmax:
+// The keys go by in steps of 32.  A step's K and V travel from the pool straight
+// into LDS (gfx950 buffer loads to LDS, 16 bytes a lane: no registers, no vector
+// instructions on the way), two steps ahead, in a ring of three LDS stages, and
+// every wave folds the step into its rows with an online softmax:
 //   S^T = K Q^T        16x16x32 matrix cores, 16 keys x 16 rows per product
 //   O^T += V^T P^T     16x16x32 matrix cores over all 32 keys of the step, P split
 //                      into high and low 16-bit parts so that it keeps fp32 accuracy
-// LDS layouts (rows padded so that the lanes of one read hit distinct banks):
-//   K: [32 keys][D] as in the pool tile, rows padded by 32 bytes
-//   V: [D][4 groups][8], rows padded by 16 bytes: group g holds keys 4g..4g+3 of the step's first 16 keys,
-//      then keys 16+4g..16+4g+3 -- exactly the 8 keys whose probabilities lane group
-//      g holds after the score product, so one 16-byte read is one matrix-core operand.
+// The two score products of a step take the keys in the order that makes each
+// lane's eight probabilities the eight consecutive keys of one 16-byte V chunk:
+// product h (0, 1) has key 8 (i / 4) + 4 h + i % 4 as its row i, so lane group g
+// ends up with keys 8 g .. 8 g + 3 from product 0 and 8 g + 4 .. 8 g + 7 from
+// product 1 (a sum over keys does not care about their order).
+// LDS layouts of a stage:
+//   K: [32 keys][D / 8 chunks of 16 bytes], chunk c of key row r stored at position
+//      c ^ f(r): the 16 rows one score operand read touches then fall on distinct
+//      banks (f: two bits of the row within its group of four, two of its group of
+//      eight)
+//   V: [2 halves of 16 keys][2 chunks of 8 keys][D] x 16 bytes: one 16-byte read is
+//      one matrix-core operand (8 keys of one head_dim row), and the 16 lanes of one
+//      read take 256 consecutive bytes.
 #pragma once
 
 #include "device.h"
@@ -36,34 +45,50 @@ constexpr int NH = 2;                  // 16-row tiles per wave
 constexpr int ROWS_PER_WAVE = 16 * NH;
 constexpr int ROWS_PER_WG = NW * ROWS_PER_WAVE;
 constexpr int KSTEP = 2 * kTileTokens; // keys per step: two 16-key halves
+constexpr int kStages = 3;             // LDS ring: the step being folded and two in flight
 
 template <int D>
 struct ChunkLds {
-    // K rows padded by 32 bytes: the 32 lanes of a 16-byte K read (16 key rows x two
-    // 16-byte columns) then fall on distinct banks; with 16 bytes of padding two of
-    // them shared banks (MI355X counters on the long mixed batch: LDS bank-conflict
-    // cycles 4.5e7 -> 2.7e7)
-    static constexpr int KROW = D * 2 + 32;      // bytes per key row of K
-    static constexpr int VROW = 4 * 16 + 16;     // bytes per head_dim row of V
-    static constexpr int KBYTES = KSTEP * KROW;
-    static constexpr int VBYTES = D * VROW;
+    static constexpr int KCH = D / 8;                 // 16-byte chunks per key row
+    static constexpr int KBYTES = KSTEP * D * 2;      // K of one step
+    static constexpr int VBYTES = KSTEP * D * 2;      // V of one step
     static constexpr int STAGE = KBYTES + VBYTES;
-    static constexpr int CHUNKS = KSTEP * D * 2 / 16 / (NW * 64);  // 16-byte K (and V) pieces per thread
+    // 1 KiB loads-to-LDS (64 lanes x 16 bytes) per step, and per wave
+    static constexpr int KLOADS = KBYTES / 1024, VLOADS = VBYTES / 1024;
+    static constexpr int KLOADS_W = KLOADS / NW, VLOADS_W = VLOADS / NW;
+    static_assert(KLOADS % NW == 0 && VLOADS % NW == 0, "every wave moves the same share");
+    // position of chunk c of key row r
+    static __device__ __forceinline__ int kpos(int r, int c) {
+        if constexpr (D == 128)
+            return c ^ ((r & 3) | (((r >> 3) & 3) << 2));
+        else
+            return c ^ (((r >> 1) & 1) | (((r >> 3) & 3) << 1));
+    }
 };
 
+typedef __attribute__((address_space(3))) void* lds_ptr_t;
+
+// gfx950 16-byte buffer load to LDS: lane t's 16 bytes at `voff` land at lds + 16 t
+// (kAux: cache policy bits)
+template <int kAux> __device__ __forceinline__ void load_to_lds(rsrc_t r, char* lds, uint32_t voff) {
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_ptr_t)lds, 16, (int)voff, 0, 0, kAux);
+}
+
 // BS: tokens per KV block (8, 16 or 32); a step's 32 keys span KSTEP / BS blocks
-// Workgroup `idx` of the chunked grid (tile, kv head, segment), with the stage
-// buffers `lds`.  With skip_single, one-row segments are left alone (the mixed
-// launch runs them as decode sequences).
+// Workgroup `idx` of the chunked grid (tile, kv head, segment), with the three LDS
+// stages st0, st1, st2 (ChunkLds<D>::STAGE bytes each; three distinct LDS
+// variables, so that the compiler can tell a stage being filled from the one being
+// read and does not make the reads wait for loads still in flight to the others).
+// With skip_single, one-row segments are left alone (the mixed launch runs them as
+// decode sequences).
 template <int K, int D, int BS>
-__device__ __forceinline__ void chunked_tile(const ChunkedParams& p, int idx, char* lds, bool skip_single) {
+__device__ __forceinline__ void chunked_tile(const ChunkedParams& p, int idx, char* st0, char* st1, char* st2,
+                                             bool skip_single) {
     constexpr int KS = D / 32;
     constexpr int DT = D / 16;
     using Lds = ChunkLds<D>;
     constexpr uint32_t kTile = BS * D * 2;  // bytes of one (block, kv head) tile
     constexpr int NBS = KSTEP / BS;         // blocks per step
-    constexpr int kPieces = (int)(kTile / 16);
-    static_assert(kPieces % 64 == 0, "a wave's 64 pieces stay inside one block");
 
     const int G = p.G;
     const int tiles = (p.max_q_len * G + ROWS_PER_WG - 1) / ROWS_PER_WG;
@@ -95,8 +120,69 @@ __device__ __forceinline__ void chunked_tile(const ChunkedParams& p, int idx, ch
     const int wave_first_pos = n - L + row0 / G;
     const int wave_last_pos = n - L + (min(row0 + ROWS_PER_WAVE, nrows) - 1) / G;
 
-    // this lane's rows: Q as the B operand of the score product; dead rows see
-    // every key with a zero query (finite, never stored)
+    // ---- loads of one step straight into an LDS stage ------------------------------
+    // Loads of blocks past the context are empty (zero bytes written, no memory
+    // access), so every step issues the same loads and the wait before a fold counts
+    // exactly: KLOADS_W + VLOADS_W per wave and step.
+    const int32_t* table = p.block_tables + (size_t)seg * p.MB;
+    // this lane's part of each of the wave's loads: K load j covers key rows 4 j'..+3
+    // (j' = the workgroup-wide load index), V load j covers 64 head_dim rows of one
+    // (half, chunk)
+    uint32_t koff[Lds::KLOADS_W], voff[Lds::VLOADS_W];
+    int kblk[Lds::KLOADS_W], vblk[Lds::VLOADS_W];
+#pragma unroll
+    for (int j = 0; j < Lds::KLOADS_W; ++j) {
+        const int jj = w * Lds::KLOADS_W + j;
+        const int rows_per_load = 64 / Lds::KCH;
+        const int r = jj * rows_per_load + lane / Lds::KCH;  // key row in the step
+        const int c = Lds::kpos(r, lane % Lds::KCH);        // the chunk this slot holds
+        kblk[j] = r / BS;
+        koff[j] = (uint32_t)((r % BS) * D * 2 + c * 16);
+    }
+#pragma unroll
+    for (int j = 0; j < Lds::VLOADS_W; ++j) {
+        const int jj = w * Lds::VLOADS_W + j;
+        const int slot = jj * 64 + lane;  // [half][chunk][d]
+        const int d = slot % D, hc = slot / D;
+        const int key = 8 * hc;           // first key of the chunk within the step
+        vblk[j] = key / BS;
+        voff[j] = (uint32_t)(d * BS * 2 + (key % BS) * 2);
+    }
+    auto issue = [&](int step, char* stage) {
+        char* kl = stage;
+        char* vl = kl + Lds::KBYTES;
+        const int b0 = step * NBS;
+        rsrc_t kr[NBS], vr[NBS];
+#pragma unroll
+        for (int b = 0; b < NBS; ++b) {
+            const bool live = b0 + b < nblk;
+            const int ph = live ? scalar_load(table, (size_t)uniform(b0 + b)) : 0;
+            const size_t t = ((size_t)ph * p.Hkv + kvh) * kTile;
+            kr[b] = tile_rsrc((const char*)p.kc + t, live ? kTile : 0);
+            vr[b] = tile_rsrc((const char*)p.vc + t, live ? kTile : 0);
+        }
+#pragma unroll
+        for (int j = 0; j < Lds::KLOADS_W; ++j) {
+            rsrc_t r = kr[0];
+#pragma unroll
+            for (int b = 1; b < NBS; ++b)
+                if (uniform(kblk[j]) == b) r = kr[b];
+            load_to_lds<kNonTemporal>(r, kl + (w * Lds::KLOADS_W + j) * 1024, koff[j]);
+        }
+        // V chunks are 16 of the 32 bytes of a head_dim row (block size 16 or 32): the
+        // other half is read by the neighbouring load, so V keeps the default policy
+#pragma unroll
+        for (int j = 0; j < Lds::VLOADS_W; ++j) {
+            rsrc_t r = vr[0];
+#pragma unroll
+            for (int b = 1; b < NBS; ++b)
+                if (uniform(vblk[j]) == b) r = vr[b];
+            load_to_lds<BS == 8 ? kNonTemporal : 0>(r, vl + (w * Lds::VLOADS_W + j) * 1024, voff[j]);
+        }
+    };
+
+    // ---- this lane's rows: Q as the B operand of the score product; dead rows see
+    // every key with a zero query (finite, never stored) ------------------------------
     int pos[NH];
     uint4 qv[NH][KS];
     const uint16_t* qp = (const uint16_t*)p.q;
@@ -122,105 +208,50 @@ __device__ __forceinline__ void chunked_tile(const ChunkedParams& p, int idx, ch
         for (int dt = 0; dt < DT; ++dt) acc[ht][dt] = f32x4{0.f, 0.f, 0.f, 0.f};
     }
 
-    // ---- staging: this thread's 16-byte pieces of K and V for one step -------------
-    const int32_t* table = p.block_tables + (size_t)seg * p.MB;
-    struct Staged {
-        uint4 k[Lds::CHUNKS], v[Lds::CHUNKS];
-    };
-    // loads of blocks past the context are empty (zero bytes, no memory access), so
-    // every step issues the same loads and the wait before staging counts exactly
-    auto fetch = [&](int step, Staged& r) {
-        const int b0 = step * NBS;
-        rsrc_t kr[NBS], vr[NBS];
-#pragma unroll
-        for (int b = 0; b < NBS; ++b) {
-            const bool live = b0 + b < nblk;
-            const int ph = live ? scalar_load(table, (size_t)uniform(b0 + b)) : 0;
-            const size_t t = ((size_t)ph * p.Hkv + kvh) * kTile;
-            kr[b] = tile_rsrc((const char*)p.kc + t, live ? kTile : 0);
-            vr[b] = tile_rsrc((const char*)p.vc + t, live ? kTile : 0);
-        }
-#pragma unroll
-        for (int i = 0; i < Lds::CHUNKS; ++i) {
-            const int c = tid + i * NW * 64;  // piece c of the step lies in block c / kPieces
-            const uint32_t off = (uint32_t)(c % kPieces) * 16;
-            // a wave's 64 pieces never straddle two blocks: the block is wave-uniform,
-            // and picking its resources is a chain of scalar selects
-            const int blk = uniform(c / kPieces);
-            rsrc_t k = kr[0], v = vr[0];
-#pragma unroll
-            for (int b = 1; b < NBS; ++b)
-                if (blk == b) {
-                    k = kr[b];
-                    v = vr[b];
-                }
-            r.k[i] = stream_load16(k, off);
-            r.v[i] = stream_load16(v, off);
-        }
-    };
-    auto stage = [&](int step, const Staged& r, int buf) {
-        char* kl = lds + buf * Lds::STAGE;
-        char* vl = kl + Lds::KBYTES;
-#pragma unroll
-        for (int i = 0; i < Lds::CHUNKS; ++i) {
-            const int c = tid + i * NW * 64;
-            const int blk = c / kPieces;
-            const int off = (c % kPieces) * 16;
-            // K: key row (within the step), 16-byte column
-            const int key = blk * BS + off / (D * 2);
-            *(uint4*)(kl + key * Lds::KROW + off % (D * 2)) = r.k[i];
-            // V: head_dim row d, keys kk .. kk+7 of the step (8 h .. 8 h + 7 of block
-            // blk); slots past the context may hold anything and are zeroed
-            const int d = off / (BS * 2);
-            const int h = (off % (BS * 2)) / 16;
-            const int kk = blk * BS + 8 * h;
-            uint4 v = r.v[i];
-            const int tok0 = step * KSTEP + kk;
-            if (tok0 + 8 > n) {
-                uint32_t u[4] = {v.x, v.y, v.z, v.w};
-#pragma unroll
-                for (int e = 0; e < 8; ++e)
-                    if (tok0 + e >= n) u[e / 2] &= (e & 1) ? 0x0000ffffu : 0xffff0000u;
-                v = make_uint4(u[0], u[1], u[2], u[3]);
-            }
-            // row d of the LDS V tile: 16-byte chunk j holds keys 4j .. 4j+3 of the
-            // step's first 16-key half, then the same keys of its second half
-            const int jj = (kk % kTileTokens) / 4;
-            char* vrow = vl + d * Lds::VROW + (kk / kTileTokens) * 8;
-            *(uint2*)(vrow + jj * 16) = make_uint2(v.x, v.y);
-            *(uint2*)(vrow + (jj + 1) * 16) = make_uint2(v.z, v.w);
-        }
-    };
-
     // ---- one step: 32 keys into this wave's 32 rows ----------------------------------
-    auto fold = [&](int step, int buf) {
-        const char* kl = lds + buf * Lds::STAGE;
+    auto fold = [&](int step, const char* stage) {
+        const char* kl = stage;
         const char* vl = kl + Lds::KBYTES;
         const int key0 = step * KSTEP;
-        // four independent score chains (2 key halves x 2 row tiles) per k-step, so
-        // consecutive matrix-core products never wait on each other
+        // four independent score chains (2 key sets x 2 row tiles) per k-step, so
+        // consecutive matrix-core products never wait on each other; key set h takes
+        // key 8 (col / 4) + 4 h + col % 4 as its row col
         uint4 kf[2][KS];
 #pragma unroll
-        for (int kh = 0; kh < 2; ++kh)
+        for (int h = 0; h < 2; ++h) {
+            const int r = 8 * (col >> 2) + 4 * h + (col & 3);
 #pragma unroll
             for (int ks = 0; ks < KS; ++ks)
-                kf[kh][ks] = *(const uint4*)(kl + (kh * kTileTokens + col) * Lds::KROW + (gq + 4 * ks) * 16);
+                kf[h][ks] = *(const uint4*)(kl + r * (D * 2) + Lds::kpos(r, gq + 4 * ks) * 16);
+        }
         f32x4 sc[2][NH];
 #pragma unroll
-        for (int kh = 0; kh < 2; ++kh)
+        for (int h = 0; h < 2; ++h)
 #pragma unroll
-            for (int ht = 0; ht < NH; ++ht) sc[kh][ht] = f32x4{0.f, 0.f, 0.f, 0.f};
+            for (int ht = 0; ht < NH; ++ht) sc[h][ht] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int ks = 0; ks < KS; ++ks)
 #pragma unroll
-            for (int kh = 0; kh < 2; ++kh)
+            for (int h = 0; h < 2; ++h)
 #pragma unroll
-                for (int ht = 0; ht < NH; ++ht) sc[kh][ht] = mma_16x16x32<K>(kf[kh][ks], qv[ht][ks], sc[kh][ht]);
-        // V fragments, read while the first softmax runs
+                for (int ht = 0; ht < NH; ++ht) sc[h][ht] = mma_16x16x32<K>(kf[h][ks], qv[ht][ks], sc[h][ht]);
+        // V fragments: head_dim row 16 dt + col, keys 8 gq .. 8 gq + 7 (half gq / 2,
+        // chunk gq % 2), read while the first softmax runs
         uint4 vf[DT];
 #pragma unroll
-        for (int dt = 0; dt < DT; ++dt) vf[dt] = *(const uint4*)(vl + (dt * 16 + col) * Lds::VROW + gq * 16);
-        // keys of this lane's eight scores: key0 + 4 gq + j and key0 + 16 + 4 gq + j
+        for (int dt = 0; dt < DT; ++dt) vf[dt] = *(const uint4*)(vl + (gq * D + dt * 16 + col) * 16);
+        // slots past the context may hold anything (NaN): zero them, last step only
+        if (key0 + KSTEP > n) {
+#pragma unroll
+            for (int dt = 0; dt < DT; ++dt) {
+                uint32_t u[4] = {vf[dt].x, vf[dt].y, vf[dt].z, vf[dt].w};
+#pragma unroll
+                for (int e = 0; e < 8; ++e)
+                    if (key0 + 8 * gq + e >= n) u[e / 2] &= (e & 1) ? 0x0000ffffu : 0xffff0000u;
+                vf[dt] = make_uint4(u[0], u[1], u[2], u[3]);
+            }
+        }
+        // keys of this lane's eight scores: key0 + 8 gq + j (set 0), key0 + 8 gq + 4 + j (set 1)
         const bool masked = key0 + KSTEP - 1 > wave_first_pos;
         const float c = p.scale_log2;
         // row tile by row tile: the P.V products of one tile run on the matrix
@@ -235,10 +266,8 @@ __device__ __forceinline__ void chunked_tile(const ChunkedParams& p, int idx, ch
             }
             if (masked) {
 #pragma unroll
-                for (int j = 0; j < 4; ++j) {
-                    if (key0 + 4 * gq + j > pos[ht]) s[j] = kNegInf;
-                    if (key0 + kTileTokens + 4 * gq + j > pos[ht]) s[4 + j] = kNegInf;
-                }
+                for (int j = 0; j < 8; ++j)
+                    if (key0 + 8 * gq + j > pos[ht]) s[j] = kNegInf;
             }
             float bm = fmaxf(fmaxf(fmaxf(s[0], s[1]), fmaxf(s[2], s[3])), fmaxf(fmaxf(s[4], s[5]), fmaxf(s[6], s[7])));
             bm = xor_max(bm, 16);
@@ -274,25 +303,32 @@ __device__ __forceinline__ void chunked_tile(const ChunkedParams& p, int idx, ch
         }
     };
 
-    // step s lives in LDS buffer s % 2; its loads were issued two steps earlier
-    // into register set s % 2
-    Staged r0, r1;
-    fetch(0, r0);
-    fetch(1, r1);
-    stage(0, r0, 0);
-    __syncthreads();
-    for (int step = 0; step < nsteps; step += 2) {
-        fetch(step + 2, r0);
+    // Step s lives in LDS stage s % 3; its loads were issued two steps earlier.  Before
+    // folding step s: wait until this wave's loads of step s have landed (those of
+    // step s + 1 may stay in flight), then a workgroup barrier, after which every
+    // wave's loads of step s are in LDS and every wave has finished folding step
+    // s - 1 -- so stage (s + 2) % 3 is free for the loads of step s + 2.  Plain
+    // barriers: the loads to LDS are waited for explicitly, and no other LDS store
+    // happens in the loop.
+    constexpr int kPerStep = Lds::KLOADS_W + Lds::VLOADS_W;
+    // fold step s from stage `cur` after issuing the loads of step s + 2 into `next`
+    auto step_once = [&](int s, const char* cur, char* next) {
+        vm_wait_le<kPerStep>();
+        __builtin_amdgcn_s_barrier();
+        issue(s + 2, next);
         // a wave whose rows all lie before this step's first key has nothing to fold
-        if (wave_live && step * KSTEP <= wave_last_pos) fold(step, 0);
-        stage(step + 1, r1, 1);
-        __syncthreads();
+        if (wave_live && s * KSTEP <= wave_last_pos) fold(s, cur);
+    };
+    issue(0, st0);
+    issue(1, st1);
+    for (int step = 0; step < nsteps; step += kStages) {
+        step_once(step, st0, st2);
         if (step + 1 >= nsteps) break;
-        fetch(step + 3, r1);
-        if (wave_live && (step + 1) * KSTEP <= wave_last_pos) fold(step + 1, 1);
-        stage(step + 2, r0, 0);
-        __syncthreads();
+        step_once(step + 1, st1, st0);
+        if (step + 2 >= nsteps) break;
+        step_once(step + 2, st2, st1);
     }
+    vm_wait_le<0>();  // no load to LDS outlives the workgroup
     if (!wave_live) return;
 
 #pragma unroll
@@ -314,9 +350,11 @@ __device__ __forceinline__ void chunked_tile(const ChunkedParams& p, int idx, ch
 
 template <int K, int D, int BS>
 __global__ __launch_bounds__(NW * 64, 2) void chunked_fa(ChunkedParams p) {
-    __shared__ __attribute__((aligned(16))) char lds[2 * ChunkLds<D>::STAGE];
+    __shared__ __attribute__((aligned(16))) char st0[ChunkLds<D>::STAGE];
+    __shared__ __attribute__((aligned(16))) char st1[ChunkLds<D>::STAGE];
+    __shared__ __attribute__((aligned(16))) char st2[ChunkLds<D>::STAGE];
     if (contract_broken(p.guard)) return;
-    chunked_tile<K, D, BS>(p, blockIdx.x, lds, false);
+    chunked_tile<K, D, BS>(p, blockIdx.x, st0, st1, st2, false);
 }
 
 }  // namespace

@@ -29,13 +29,15 @@ constexpr int kMixedRing = 3;
 
 template <class Loop, int K, int D, int BS>
 __global__ __launch_bounds__(NW * 64, 2) void mixed_kernel(DecodeParams dp, ChunkedParams cp, int decode_wgs) {
-    __shared__ __attribute__((aligned(16))) char lds[2 * ChunkLds<D>::STAGE];
+    __shared__ __attribute__((aligned(16))) char st0[ChunkLds<D>::STAGE];
+    __shared__ __attribute__((aligned(16))) char st1[ChunkLds<D>::STAGE];
+    __shared__ __attribute__((aligned(16))) char st2[ChunkLds<D>::STAGE];
     if (contract_broken(dp.guard)) return;
     if ((int)blockIdx.x < decode_wgs) {
         const long long w = (long long)blockIdx.x * NW + uniform((int)(threadIdx.x >> 6));
         decode_split_wave<Loop, kMixedRing>(dp, w, (long long)decode_wgs * NW);
     } else {
-        chunked_tile<K, D, BS>(cp, (int)blockIdx.x - decode_wgs, lds, true);
+        chunked_tile<K, D, BS>(cp, (int)blockIdx.x - decode_wgs, st0, st1, st2, true);
     }
 }
 
