@@ -269,13 +269,14 @@ __device__ __forceinline__ void chunked_tile(const ChunkedParams& p, int idx, ch
                 for (int j = 0; j < 8; ++j)
                     if (key0 + 8 * gq + j > pos[ht]) s[j] = kNegInf;
             }
-            float bm = fmaxf(fmaxf(fmaxf(s[0], s[1]), fmaxf(s[2], s[3])), fmaxf(fmaxf(s[4], s[5]), fmaxf(s[6], s[7])));
-            bm = xor_max(bm, 16);
-            bm = xor_max(bm, 32);
-            bm *= c;  // the scale is positive: the max of the scaled scores
+            // this lane's maximum of its eight scaled scores (the scale is positive); only
+            // when one exceeds the reference by the slack is the row maximum over the
+            // four lanes of the row needed
+            const float lm =
+                fmaxf(fmaxf(fmaxf(s[0], s[1]), fmaxf(s[2], s[3])), fmaxf(fmaxf(s[4], s[5]), fmaxf(s[6], s[7]))) * c;
             // key 0 is visible to every row, so m is finite from the first step on
-            if (__ballot(bm > m[ht] + kRescaleSlack)) {
-                const float mn = fmaxf(m[ht], bm);
+            if (__ballot(lm > m[ht] + kRescaleSlack)) {
+                const float mn = fmaxf(m[ht], xor_max(xor_max(lm, 16), 32));
                 const float alpha = fast_exp2(m[ht] - mn);
                 l[ht] *= alpha;
 #pragma unroll
