@@ -178,14 +178,18 @@ __device__ __forceinline__ int sequence_of_unit(const long long* starts, int S, 
 //  * at least one stream per four waves (many short streams, each cut into a couple of
 //    pieces): one workgroup per owning wave merges every head of its stream
 //    (decode_merge_stream);
-//  * otherwise one workgroup per (stream, head) (decode_merge_head), with 2 groups of
-//    128 lanes, or 8 when a stream averages more than 64 pieces.
+//  * otherwise one workgroup per (stream, head) (decode_merge_head) with 2 groups of
+//    128 lanes, or 8 when a stream averages more than 64 pieces -- and then, when there
+//    are fewer than 64 (stream, head) pairs (one or two long sequences), one workgroup
+//    per quarter of a (stream, head) with 32 groups of 32 lanes instead: four times the
+//    workgroups, each group folding a handful of pieces in one round of loads.
 struct MergeChoice {
-    int kind;  // 0: per stream, 1: per head with 2 groups, 2: per head with 8 groups
+    int kind;  // 0: per stream; per head with 1: 2 groups, 2: 8 groups; 3: per quarter head, 32 groups
 };
 inline MergeChoice merge_choice(long long streams, int cap, int waves) {
     if (streams * 4 >= waves) return {0};
-    return {streams * 64 >= waves ? 1 : 2};
+    if (streams * 64 >= waves) return {1};
+    return {streams * cap < 64 ? 3 : 2};
 }
 
 // Waves of the balanced split that take units: all N launched, unless the batch has
@@ -431,14 +435,20 @@ __global__ __launch_bounds__(64, Loop::kWaves) void decode_fixed(DecodeParams p)
 
 // ---------------------------------------------------------------------------------------
 // balanced split, many short streams: workgroup w merges all heads of the stream
-// whose merge note wave w left (see MergeNote), if any (four output elements per
-// thread in flight at once):
+// whose merge note wave w left (see MergeNote), if any:
 //   o = sum_i 2^(m_i - M) acc_i / sum_i 2^(m_i - M) l_i.
 // Its pieces are the waves w0 .. w whose unit ranges cut the stream (w0's last
 // record, then slot 0 of the others); when U < N each unit sits alone in its wave.
+// A thread takes four consecutive head_dim elements of one head, eight pieces at a
+// time with all their loads in flight; the workgroup has
+// as many threads as the stream has such quads (up to kMergeStreamThreads; 1024 for
+// the 32 heads of an MQA stream at head_dim 128), so that one round of loads merges
+// a stream of up to eight pieces.
 // ---------------------------------------------------------------------------------------
+constexpr int kMergeStreamThreads = 1024;
+
 template <int K, int HT>
-__global__ __launch_bounds__(256) void decode_merge_stream(DecodeParams p, int split_waves) {
+__global__ __launch_bounds__(kMergeStreamThreads) void decode_merge_stream(DecodeParams p, int split_waves) {
     if (contract_broken(p.guard)) return;
     // the note, through scalar loads (fields: a, U as int64, then s, c, nb)
     const int32_t* nt = (const int32_t*)(p.notes + blockIdx.x);
@@ -461,23 +471,30 @@ __global__ __launch_bounds__(256) void decode_merge_stream(DecodeParams p, int s
         const long long w = U >= N ? w0 + i : wave_of(a + i, U, N);
         return p.ws + (size_t)w * 2 * rec;  // slot 0: that wave's first segment
     };
-    // one pass over the pieces, eight at a time so that their loads are in flight
-    // together: (M, L, O) folded online, rescaled by 2^(M_old - M_new)
+    // one online pass over the pieces, eight at a time: (M, L, O) rescaled by
+    // 2^(M_old - M_new)
     constexpr int CH = 8;
-    auto merge_elem = [&](int e) {
-        const int h = e / D, d = e - h * D;
-        float M = kNegInf, L = 0.f, O = 0.f;
+    const int quads = D / 4;
+    const int n = hd.nh * quads;
+    for (int u = threadIdx.x; u < n; u += blockDim.x) {
+        const int h = u / quads, d = (u - h * quads) * 4;
+        float M = kNegInf, L = 0.f;
+        f32x4 O = {0.f, 0.f, 0.f, 0.f};
         for (long long i0 = 0; i0 < count; i0 += CH) {
-            float mv[CH], lv[CH], av[CH];
+            float mv[CH], lv[CH];
+            f32x4 av[CH];
 #pragma unroll
             for (int j = 0; j < CH; ++j) {
                 mv[j] = kNegInf;
-                lv[j] = av[j] = 0.f;
+                lv[j] = 0.f;
+                av[j] = f32x4{0.f, 0.f, 0.f, 0.f};
                 if (i0 + j < count) {
                     const float* r = record(i0 + j);
                     mv[j] = r[cap * D + h];
                     lv[j] = r[cap * D + cap + h];
-                    av[j] = r[h * D + d];
+                    // records are 8-byte aligned (cap (D + 2) floats each)
+                    const f32x2 a0 = *(const f32x2*)(r + h * D + d), a1 = *(const f32x2*)(r + h * D + d + 2);
+                    av[j] = f32x4{a0[0], a0[1], a1[0], a1[1]};
                 }
             }
             float mn = M;
@@ -494,36 +511,37 @@ __global__ __launch_bounds__(256) void decode_merge_stream(DecodeParams p, int s
             }
             M = mn;
         }
-        store_elem<K>(p.out, (orow * p.Hq + hd.head0 + h) * D + d, L > 0.f ? O / L : 0.f);
-    };
-    const int n = hd.nh * D;
-    if (n <= 2 * (int)blockDim.x) {  // few heads: at most two elements per thread
-        for (int e = threadIdx.x; e < n; e += blockDim.x) merge_elem(e);
-    } else {                          // many heads: four elements per thread in flight at once
-#pragma unroll 4
-        for (int e = threadIdx.x; e < n; e += blockDim.x) merge_elem(e);
+        const float inv = L > 0.f ? 1.f / L : 0.f;
+        const size_t e = (orow * p.Hq + hd.head0 + h) * D + d;
+#pragma unroll
+        for (int k = 0; k < 4; ++k) store_elem<K>(p.out, e + k, O[k] * inv);
     }
 }
 
 // ---------------------------------------------------------------------------------------
-// merge of the pieces of a stream, one query head per workgroup:
+// merge of the pieces of a stream, one query head (or a 1/DS share of its head_dim)
+// per workgroup:
 //   o = sum_i 2^(m_i - M) acc_i / sum_i 2^(m_i - M) l_i.
 // Pieces: the fixed partitions 0 .. nparts-1 of the stream, or, for the balanced
 // split, the waves w0 .. w1 whose unit ranges cut the stream (w0's last record,
 // then slot 0 of the others; when U < N each unit sits alone in its own wave).
-// NG groups x 128 head_dim lanes (NG = 2, or 8 for streams of hundreds of pieces);
-// group g folds pieces g, g+NG, ... in one online pass, kChunk pieces at a time with
-// all their loads in flight, (M, L, O) rescaled by 2^(M_old - M_new); the groups are
-// joined through LDS at the end.
+// NG groups x (128 / DS) head_dim lanes; group g folds pieces g, g+NG, ... in one
+// online pass, kChunk pieces at a time with all their loads in flight, (M, L, O)
+// rescaled by 2^(M_old - M_new); the groups are joined through LDS at the end.
+// (NG, DS) = (2, 1) for streams of tens of pieces, (8, 1) for hundreds, (32, 4) for
+// hundreds of pieces of fewer than 64 (stream, head) pairs (see merge_choice).
 // ---------------------------------------------------------------------------------------
-template <int K, int HT, int NG>
-__global__ __launch_bounds__(NG * 128) void decode_merge_head(DecodeParams p, int split_waves) {
-    constexpr int kChunk = 16;  // pieces per group in flight at once
-    __shared__ float other[NG - 1][128 + 2];
+template <int K, int HT, int NG, int DS>
+__global__ __launch_bounds__(NG * 128 / DS) void decode_merge_head(DecodeParams p, int split_waves) {
+    constexpr int kChunk = 16;     // pieces per group in flight at once
+    constexpr int GL = 128 / DS;   // head_dim lanes of a group
+    __shared__ float other[NG - 1][GL + 2];
     if (contract_broken(p.guard)) return;
     const int NS = p.Hkv * p.chunks;
     const int cap = min(p.G, HT);
     int idx = blockIdx.x;
+    const int part = idx % DS;
+    idx /= DS;
     const int h = idx % cap;
     idx /= cap;
     const int c = idx % NS;
@@ -560,8 +578,11 @@ __global__ __launch_bounds__(NG * 128) void decode_merge_head(DecodeParams p, in
         if (i == 0) return first;
         return p.ws + (size_t)(U >= N ? w0 + i : wave_of(a + i, U, N)) * 2 * rec;
     };
-    const int g = tid >> 7, d = tid & 127;
-    const int dd = d < D ? d : 0;  // lanes past head_dim read element 0 and store nothing
+    const int g = tid / GL, lane = tid - g * GL;
+    const int dn = D / DS;             // head_dim elements of this workgroup
+    const int d = part * dn + lane;
+    const bool dlive = lane < dn;
+    const int dd = dlive ? d : 0;      // lanes past this share read element 0 and store nothing
     float M = kNegInf, L = 0.f, O = 0.f;
     for (long long i0 = g; i0 < count; i0 += (long long)NG * kChunk) {
         float mv[kChunk], lv[kChunk], av[kChunk];
@@ -594,25 +615,25 @@ __global__ __launch_bounds__(NG * 128) void decode_merge_head(DecodeParams p, in
     // join groups 1 .. NG-1 into group 0 (every piece has a finite m, so a group's M is
     // finite whenever it had a piece; a group without pieces keeps M = -inf, L = O = 0)
     if (g > 0) {
-        other[g - 1][d] = O;
-        if (d == 0) {
-            other[g - 1][128] = M;
-            other[g - 1][129] = L;
+        other[g - 1][lane] = O;
+        if (lane == 0) {
+            other[g - 1][GL] = M;
+            other[g - 1][GL + 1] = L;
         }
     }
     __syncthreads();
-    if (g == 0 && d < D) {
+    if (g == 0 && dlive) {
         float mn = M;
-#pragma unroll
-        for (int k = 0; k < NG - 1; ++k) mn = fmaxf(mn, other[k][128]);
+#pragma unroll 8
+        for (int k = 0; k < NG - 1; ++k) mn = fmaxf(mn, other[k][GL]);
         const float s0 = M == kNegInf ? 0.f : fast_exp2(M - mn);
         float Lt = L * s0, Ot = O * s0;
-#pragma unroll
+#pragma unroll 8
         for (int k = 0; k < NG - 1; ++k) {
-            const float Mk = other[k][128];
+            const float Mk = other[k][GL];
             const float sk = Mk == kNegInf ? 0.f : fast_exp2(Mk - mn);
-            Lt += other[k][129] * sk;
-            Ot += other[k][d] * sk;
+            Lt += other[k][GL + 1] * sk;
+            Ot += other[k][lane] * sk;
         }
         store_elem<K>(p.out, (orow * p.Hq + hd.head0 + h) * D + d, Lt > 0.f ? Ot / Lt : 0.f);
     }
@@ -713,9 +734,18 @@ void launch_split_merge(const DecodeParams& p, int NS, int cap, int waves, hipSt
     const long long streams = (long long)p.S * NS;
     const unsigned per_head = (unsigned)(streams * cap);
     switch (merge_choice(streams, cap, waves).kind) {
-    case 0: hipLaunchKernelGGL((decode_merge_stream<K, HT>), dim3((unsigned)waves), dim3(256), 0, st, p, waves); break;
-    case 1: hipLaunchKernelGGL((decode_merge_head<K, HT, 2>), dim3(per_head), dim3(256), 0, st, p, waves); break;
-    default: hipLaunchKernelGGL((decode_merge_head<K, HT, 8>), dim3(per_head), dim3(1024), 0, st, p, waves); break;
+    case 0: {
+        // one thread per four head_dim elements of the stream's heads (a multiple of 64)
+        const int quads = cap * p.D / 4;
+        const int threads = quads >= kMergeStreamThreads ? kMergeStreamThreads : (quads + 63) / 64 * 64;
+        hipLaunchKernelGGL((decode_merge_stream<K, HT>), dim3((unsigned)waves), dim3(threads), 0, st, p, waves);
+        break;
+    }
+    case 1: hipLaunchKernelGGL((decode_merge_head<K, HT, 2, 1>), dim3(per_head), dim3(256), 0, st, p, waves); break;
+    case 2: hipLaunchKernelGGL((decode_merge_head<K, HT, 8, 1>), dim3(per_head), dim3(1024), 0, st, p, waves); break;
+    default:
+        hipLaunchKernelGGL((decode_merge_head<K, HT, 32, 4>), dim3(per_head * 4), dim3(1024), 0, st, p, waves);
+        break;
     }
 }
 
@@ -750,7 +780,7 @@ hipError_t run(const DecodeParams& p0, bool split, bool shallow, int slot, hipSt
     const int cap = p.G < Loop::HT ? p.G : Loop::HT;
     const unsigned per_head = (unsigned)((long long)p.S * NS * cap);
     if (!split && cap > 8)  // many heads, hundreds of partitions: the online per-head merge
-        hipLaunchKernelGGL((decode_merge_head<K, Loop::HT, 2>), dim3(per_head), dim3(256), 0, st, p, 0);
+        hipLaunchKernelGGL((decode_merge_head<K, Loop::HT, 2, 1>), dim3(per_head), dim3(256), 0, st, p, 0);
     else if (!split)
         hipLaunchKernelGGL((decode_merge_fixed<K, Loop::HT>), dim3(per_head), dim3(256), 0, st, p);
     else

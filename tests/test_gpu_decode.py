@@ -261,9 +261,12 @@ def test_balanced_split_edges(depth, dtype, G, Hkv, D, ctx):
     ("f16", 1, 8, [20000]),            # ~128 pieces per stream: per-head merge, 8 groups
     ("bf16", 4, 8, [300] * 300),       # many streams: per-stream merge
     ("bf16", 32, 1, [300] * 300),      # many MQA streams: per-stream merge of 32 heads
+    ("bf16", 32, 1, [20000, 30000, 9000, 25000]),  # 4 long MQA streams, 128 (stream, head) pairs: 8 groups
+    ("bf16", 32, 1, [60000]),          # one long MQA stream: a quarter of a head per workgroup
 ])
 def test_long_streams_and_all_split_merges(dtype, G, Hkv, ctx):
     """Every merge of the balanced split (per stream for many short streams, per head
-    with two or eight groups for few long ones) against the oracle."""
+    with two or eight groups for few long ones, per quarter head for one or two long
+    sequences) against the oracle."""
     case = make_decode_case([47, G, len(ctx)], dtype, ctx, G * Hkv, Hkv, 128)
     check_close(run_decode(case), oracle_decode_case(case), dtype, f"long streams {ctx[:2]}")
