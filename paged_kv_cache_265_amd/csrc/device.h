@@ -164,14 +164,17 @@ template <int kAux> __device__ __forceinline__ uint2 policy_load8(rsrc_t r, uint
     return make_uint2(x.x, x.y);
 }
 
-// Fence between matrix-core products and the first vector-ALU read of their result:
-// nothing is scheduled across it, and 24 wait states separate the two.  Without it
-// the decode loops, sharing a SIMD with other waves' matrix-core work, gave
-// occasional last-bit differences between runs (the lazy softmax reference then
-// moved), which this padding removes.
+// Fence between a chain of 16x16x32 matrix-core products and the first vector-ALU
+// read of its result.  A 4-pass XDL product writing VGPRs must be followed by 8 wait
+// states before a VALU instruction reads the result on gfx950 (the compiler pads the
+// fall-through path with exactly that many).  Where the read sits at the head of a
+// block reached by a taken branch -- the softmax's unmasked path, jumped to right after
+// the score products -- this compiler inserts none: the read followed the product by a
+// single wait state, and outputs differed in their last bits from run to run.  Eight
+// wait states here, with nothing scheduled across them, cover every path.
 __device__ __forceinline__ void mfma_result_fence() {
     __builtin_amdgcn_sched_barrier(0);
-    asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7");
+    asm volatile("s_nop 7");
     __builtin_amdgcn_sched_barrier(0);
 }
 
