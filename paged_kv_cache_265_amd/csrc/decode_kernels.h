@@ -176,18 +176,23 @@ __device__ __forceinline__ int sequence_of_unit(const long long* starts, int S, 
 // Which merge joins the pieces of the balanced split, from what the host knows (the
 // streams of the batch against the split waves):
 //  * at least one stream per four waves (many short streams, each cut into a couple of
-//    pieces): one workgroup per owning wave merges every head of its stream
-//    (decode_merge_stream);
+//    pieces): one workgroup merges every head of a stream (decode_merge_stream) -- one
+//    per split wave, reading the merge note the wave left, when there are at least as
+//    many streams as waves; one per stream, finding its pieces through starts[], when
+//    there are fewer (then most waves own no stream, and a workgroup per wave would
+//    launch up to four times the workgroups, each as wide as a stream's heads);
 //  * otherwise one workgroup per (stream, head) (decode_merge_head) with 2 groups of
 //    128 lanes, or 8 when a stream averages more than 64 pieces -- and then, when there
 //    are fewer than 64 (stream, head) pairs (one or two long sequences), one workgroup
 //    per quarter of a (stream, head) with 32 groups of 32 lanes instead: four times the
 //    workgroups, each group folding a handful of pieces in one round of loads.
 struct MergeChoice {
-    int kind;  // 0: per stream; per head with 1: 2 groups, 2: 8 groups; 3: per quarter head, 32 groups
+    // 0: per stream, a workgroup per wave; 4: per stream, a workgroup per stream;
+    // per head with 1: 2 groups, 2: 8 groups; 3: per quarter head, 32 groups
+    int kind;
 };
 inline MergeChoice merge_choice(long long streams, int cap, int waves) {
-    if (streams * 4 >= waves) return {0};
+    if (streams * 4 >= waves) return {streams >= waves ? 0 : 4};
     if (streams * 64 >= waves) return {1};
     return {streams * cap < 64 ? 3 : 2};
 }
@@ -434,9 +439,12 @@ __global__ __launch_bounds__(64, Loop::kWaves) void decode_fixed(DecodeParams p)
 }
 
 // ---------------------------------------------------------------------------------------
-// balanced split, many short streams: workgroup w merges all heads of the stream
-// whose merge note wave w left (see MergeNote), if any:
-//   o = sum_i 2^(m_i - M) acc_i / sum_i 2^(m_i - M) l_i.
+// balanced split, many short streams: a workgroup merges all heads of one stream,
+//   o = sum_i 2^(m_i - M) acc_i / sum_i 2^(m_i - M) l_i:
+// with kByStream false, workgroup w takes the stream whose merge note wave w left
+// (see MergeNote), if any; with kByStream true, workgroup b takes stream b (sequence
+// b / NS, stream b % NS), its units found through starts[] (nothing to do when one
+// wave holds the whole stream: that wave wrote its output).
 // Its pieces are the waves w0 .. w whose unit ranges cut the stream (w0's last
 // record, then slot 0 of the others); when U < N each unit sits alone in its wave.
 // A thread takes four consecutive head_dim elements of one head, eight pieces at a
@@ -447,16 +455,35 @@ __global__ __launch_bounds__(64, Loop::kWaves) void decode_fixed(DecodeParams p)
 // ---------------------------------------------------------------------------------------
 constexpr int kMergeStreamThreads = 1024;
 
-template <int K, int HT>
+template <int K, int HT, bool kByStream>
 __global__ __launch_bounds__(kMergeStreamThreads) void decode_merge_stream(DecodeParams p, int split_waves) {
     if (contract_broken(p.guard)) return;
-    // the note, through scalar loads (fields: a, U as int64, then s, c, nb)
-    const int32_t* nt = (const int32_t*)(p.notes + blockIdx.x);
-    const int ns = scalar_load(nt, 4);
-    if (ns < 0) return;
-    const long long a = scalar_load64(nt, 0), U = scalar_load64(nt, 2), N = working_waves(U, split_waves);
-    const int nc = scalar_load(nt, 5), nnb = scalar_load(nt, 6);
-    const long long w1 = blockIdx.x;
+    int ns, nc, nnb;
+    long long a, U, N, w1;
+    if constexpr (kByStream) {
+        const int NS = p.Hkv * p.chunks;
+        ns = blockIdx.x / NS;
+        nc = blockIdx.x - ns * NS;
+        if (!is_decode(p, ns)) return;
+        nnb = ntiles(p.context_lens[ns]);
+        if (nnb == 0) return;  // empty context: its zero output comes from the split kernel
+        U = p.starts[p.S];
+        N = working_waves(U, split_waves);
+        a = p.starts[ns] + (long long)nc * nnb;
+        w1 = wave_of(a + nnb - 1, U, N);
+        if (wave_of(a, U, N) == w1) return;  // written whole by one wave
+    } else {
+        // the note, through scalar loads (fields: a, U as int64, then s, c, nb)
+        const int32_t* nt = (const int32_t*)(p.notes + blockIdx.x);
+        ns = scalar_load(nt, 4);
+        if (ns < 0) return;
+        a = scalar_load64(nt, 0);
+        U = scalar_load64(nt, 2);
+        N = working_waves(U, split_waves);
+        nc = scalar_load(nt, 5);
+        nnb = scalar_load(nt, 6);
+        w1 = blockIdx.x;
+    }
     const Heads hd = stream_heads<HT>(p, nc);
     const int cap = min(p.G, HT);
     const int D = p.D;
@@ -734,11 +761,17 @@ void launch_split_merge(const DecodeParams& p, int NS, int cap, int waves, hipSt
     const long long streams = (long long)p.S * NS;
     const unsigned per_head = (unsigned)(streams * cap);
     switch (merge_choice(streams, cap, waves).kind) {
-    case 0: {
+    case 0:
+    case 4: {
         // one thread per four head_dim elements of the stream's heads (a multiple of 64)
         const int quads = cap * p.D / 4;
         const int threads = quads >= kMergeStreamThreads ? kMergeStreamThreads : (quads + 63) / 64 * 64;
-        hipLaunchKernelGGL((decode_merge_stream<K, HT>), dim3((unsigned)waves), dim3(threads), 0, st, p, waves);
+        if (merge_choice(streams, cap, waves).kind == 0)
+            hipLaunchKernelGGL((decode_merge_stream<K, HT, false>), dim3((unsigned)waves), dim3(threads), 0, st, p,
+                               waves);
+        else
+            hipLaunchKernelGGL((decode_merge_stream<K, HT, true>), dim3((unsigned)streams), dim3(threads), 0, st, p,
+                               waves);
         break;
     }
     case 1: hipLaunchKernelGGL((decode_merge_head<K, HT, 2, 1>), dim3(per_head), dim3(256), 0, st, p, waves); break;

@@ -259,8 +259,10 @@ def test_balanced_split_edges(depth, dtype, G, Hkv, D, ctx):
 @pytest.mark.parametrize("dtype,G,Hkv,ctx", [
     ("bf16", 4, 8, [32768, 5000]),     # few long streams: per-head merge, 2 groups
     ("f16", 1, 8, [20000]),            # ~128 pieces per stream: per-head merge, 8 groups
-    ("bf16", 4, 8, [300] * 300),       # many streams: per-stream merge
-    ("bf16", 32, 1, [300] * 300),      # many MQA streams: per-stream merge of 32 heads
+    ("bf16", 4, 8, [300] * 300),       # more streams than waves: per-stream merge, a workgroup per wave
+    ("bf16", 4, 8, [300] * 60),        # fewer streams than waves: per-stream merge, a workgroup per stream
+    ("bf16", 32, 1, [300] * 300),      # many MQA streams: per-stream merge of 32 heads, a workgroup per stream
+    ("bf16", 32, 1, [40] * 1100),      # more MQA streams than waves: a workgroup per wave
     ("bf16", 32, 1, [20000, 30000, 9000, 25000]),  # 4 long MQA streams, 128 (stream, head) pairs: 8 groups
     ("bf16", 32, 1, [60000]),          # one long MQA stream: a quarter of a head per workgroup
 ])
