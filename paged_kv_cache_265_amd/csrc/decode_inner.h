@@ -58,6 +58,7 @@ struct MfmaLoop {
     // flight (six tiles x 12 loads stays under the 63 outstanding loads a wave
     // can count).
     static constexpr int kWaves = (NH == 1 && D == 64) ? 2 : 1;
+    static constexpr bool kCoop = false;
     static constexpr int kRing = D == 128 ? (NH == 2 ? 6 : 5) : 3;
 
     struct Tile {
@@ -250,6 +251,10 @@ struct MfmaWideLoop {
     static constexpr int DQ = D / 32;  // 32-row head_dim tiles of the output
     static constexpr int HT = 32;
     static constexpr int kWaves = 1;
+    static constexpr int kKind = K;
+    static constexpr int kD = D;
+    // the balanced split runs this loop on cooperative workgroups (decode_split_coop)
+    static constexpr bool kCoop = true;
     // half the V loads of MfmaLoop: at head_dim 128 six tiles fit the register file
     static constexpr int kRing = D == 128 ? 6 : 8;
     static constexpr int kTileLoads = KS + DQ;
@@ -485,6 +490,7 @@ struct ValuLoop {
     static constexpr int VC = D * CPR / 64;            // V chunks per lane
     static constexpr int HT = GT;
     static constexpr int kWaves = ((D == 128 && (EB == 4 || GT >= 2)) || (EB == 4 && GT == 4)) ? 1 : 2;
+    static constexpr bool kCoop = false;
     static constexpr int kRing = 3;
 
     struct Tile {

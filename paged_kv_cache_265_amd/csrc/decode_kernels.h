@@ -218,12 +218,25 @@ __host__ __device__ __forceinline__ long long wave_of(long long u, long long U, 
 // ---------------------------------------------------------------------------------------
 // balanced split
 // ---------------------------------------------------------------------------------------
-// Wave w of the N launched (wave-uniform) takes units [w U / Nw, (w+1) U / Nw) of the
-// U units, Nw = working_waves(U, N); waves w >= Nw take none.
-template <class Loop, int R>
-__device__ __forceinline__ void decode_split_wave(const DecodeParams& p, long long w, long long N_launched) {
-    constexpr int HT = Loop::HT;
-    const int lane = lane_id();
+// A position in the unit order: tile b of stream c of sequence s (nb tiles, ctx tokens).
+struct Cursor {
+    int s, c, b, nb, ctx;
+};
+
+// the same cursor, asserted wave-uniform (so that the compiler keeps it in scalar registers)
+__device__ __forceinline__ Cursor uniform_cursor(const Cursor& x) {
+    return Cursor{uniform(x.s), uniform(x.c), uniform(x.b), uniform(x.nb), uniform(x.ctx)};
+}
+
+// Range [lo, hi) of the U units taken by split piece w of the N launched (a wave, or
+// a cooperative workgroup), Nw = working_waves(U, N): [w U / Nw, (w+1) U / Nw), empty
+// for w >= Nw; cur locates unit lo.  With `writer` (one wave per piece) also the
+// merge note of piece w, and in small batches starts[] (piece 0) and the zero
+// outputs of empty sequences s with s mod N = w.  Returns false for an empty range.
+template <int EB>
+__device__ __forceinline__ bool split_range(const DecodeParams& p, long long w, long long N_launched, int lane,
+                                            bool writer, long long& U_out, long long& lo_out, long long& hi_out,
+                                            Cursor& cur) {
     const int NS = p.Hkv * p.chunks;
     // small batches: sequence 64 j + lane's context and its first unit, in registers
     const bool small = p.S <= kInWaveSeqs;
@@ -240,14 +253,14 @@ __device__ __forceinline__ void decode_split_wave(const DecodeParams& p, long lo
             const long long incl = wave_incl_scan((long long)nb, lane);
             first[j] = (long long)NS * (tiles + incl - nb);
             tiles += uniform(read_lane64(incl, 63));
-            for (unsigned long long e = __ballot(dec && nb == 0 && s % N_launched == w); e; e &= e - 1) {
+            for (unsigned long long e = __ballot(writer && dec && nb == 0 && s % N_launched == w); e; e &= e - 1) {
                 const int se = 64 * j + __builtin_ctzll(e);
-                const size_t n16 = (size_t)p.Hq * p.D * Loop::kElemBytes / 16;
-                uint4* row = (uint4*)((char*)p.out + row_of_uniform(p, se) * p.Hq * p.D * Loop::kElemBytes);
+                const size_t n16 = (size_t)p.Hq * p.D * EB / 16;
+                uint4* row = (uint4*)((char*)p.out + row_of_uniform(p, se) * p.Hq * p.D * EB);
                 for (size_t i = lane; i < n16; i += 64) row[i] = make_uint4(0, 0, 0, 0);
             }
         }
-        if (w == 0) {
+        if (writer && w == 0) {
 #pragma unroll
             for (int j = 0; j < 4; ++j)
                 if (64 * j + lane < p.S) p.starts[64 * j + lane] = first[j];
@@ -260,15 +273,15 @@ __device__ __forceinline__ void decode_split_wave(const DecodeParams& p, long lo
     const long long U = uniform(small ? (long long)NS * tiles : p.starts[p.S]);
     const long long N = uniform(working_waves(U, N_launched));
     const long long lo = w < N ? uniform(w * U / N) : U, hi = w < N ? uniform((w + 1) * U / N) : U;
+    U_out = U;
+    lo_out = lo;
+    hi_out = hi;
     if (lo >= hi) {
-        if (lane == 0) p.notes[w] = MergeNote{0, U, -1, 0, 0, 0};
-        return;
+        if (writer && lane == 0) p.notes[w] = MergeNote{0, U, -1, 0, 0, 0};
+        return false;
     }
 
     // locate unit lo: its sequence, then its stream and tile inside the sequence
-    struct Cursor {
-        int s, c, b, nb, ctx;
-    } cur;
     {
         long long a0 = 0;  // first unit of sequence cur.s
         if (small) {
@@ -296,13 +309,28 @@ __device__ __forceinline__ void decode_split_wave(const DecodeParams& p, long lo
         cur.c = (int)(r / cur.nb);
         cur.b = (int)(r - (long long)cur.c * cur.nb);
     }
-    // merge note: this wave merges the stream it starts in when that stream began in
-    // an earlier wave and ends in this one
-    if (lane == 0) {
+    // merge note: this piece merges the stream it starts in when that stream began in
+    // an earlier piece and ends in this one
+    if (writer && lane == 0) {
         const long long a = lo - cur.b;
         const bool own = cur.b > 0 && a + cur.nb <= hi;
         p.notes[w] = MergeNote{a, U, own ? cur.s : -1, cur.c, cur.nb, 0};
     }
+    return true;
+}
+
+// Wave w of the N launched (wave-uniform) takes the units of split_range.
+template <class Loop, int R>
+__device__ __forceinline__ void decode_split_wave(const DecodeParams& p, long long w, long long N_launched) {
+    constexpr int HT = Loop::HT;
+    const int lane = lane_id();
+    const int NS = p.Hkv * p.chunks;
+    long long U, lo, hi;
+    Cursor cur;
+    if (!split_range<Loop::kElemBytes>(p, w, N_launched, lane, true, U, lo, hi, cur)) return;
+    lo = uniform(lo);
+    hi = uniform(hi);
+    cur = uniform_cursor(cur);
     auto advance = [&](Cursor& x) {
         if (++x.b < x.nb) return;
         x.b = 0;
@@ -383,6 +411,188 @@ template <class Loop, int R>
 __global__ __launch_bounds__(64, Loop::kWaves) void decode_split(DecodeParams p) {
     if (contract_broken(p.guard)) return;
     decode_split_wave<Loop, R>(p, blockIdx.x, gridDim.x);
+}
+
+// ---------------------------------------------------------------------------------------
+// cooperative balanced split (loops with 32 heads per stream): piece w is a workgroup
+// of kCoopWaves waves, one per SIMD, sharing one unit range [lo, hi); wave k folds
+// units lo + k, lo + k + kCoopWaves, ... into its own state, so that the four waves
+// stream neighbouring tiles of the same stream at the same time.  At the end of every
+// stream segment of the range the waves join their (m, l, acc) states through LDS
+// -- o = sum_k 2^(m_k - M) acc_k / sum_k 2^(m_k - M) l_k, a wave without tiles in the
+// segment contributing nothing -- and each wave writes its quarter of the heads: the
+// output when the segment is a whole stream, else the piece's record.  A stream is
+// then cut into a quarter as many pieces as with one wave per piece: fewer, smaller
+// records for the merge, and none when streams and ranges line up.
+// ---------------------------------------------------------------------------------------
+constexpr int kCoopWaves = 4;
+
+// barrier over the workgroup's LDS traffic only: waits for this wave's LDS accesses,
+// not for its global loads still in flight (a release fence would wait for those too)
+__device__ __forceinline__ void lds_barrier() {
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+}
+
+template <class Loop, int R>
+__global__ __launch_bounds__(64 * kCoopWaves, 1) void decode_split_coop(DecodeParams p) {
+    constexpr int HT = Loop::HT;
+    constexpr int D = Loop::kD;
+    constexpr int kSlot = HT * D + 2 * HT;  // acc[HT][D], m[HT], l[HT] of one wave
+    __shared__ float slot[kCoopWaves][kSlot];
+    __shared__ int used[kCoopWaves];
+    if (contract_broken(p.guard)) return;
+    const int lane = lane_id();
+    const int k = uniform((int)(threadIdx.x >> 6));
+    const long long w = blockIdx.x;
+    const int NS = p.Hkv * p.chunks;
+    long long U, lo, hi;
+    Cursor cur;
+    // the range depends on w alone: every wave of the workgroup returns here or none
+    if (!split_range<Loop::kElemBytes>(p, w, gridDim.x, lane, k == 0, U, lo, hi, cur)) return;
+    lo = uniform(lo);
+    hi = uniform(hi);
+    cur = uniform_cursor(cur);
+    auto advance = [&](Cursor& x) {
+        if (++x.b < x.nb) return;
+        x.b = 0;
+        if (++x.c < NS) return;
+        x.c = 0;
+        do {
+            ++x.s;
+            x.ctx = x.s < p.S ? dec_ctx_uniform(p, uniform(x.s)) : kTileTokens;
+            x.nb = ntiles(x.ctx);
+        } while (x.nb == 0);
+    };
+    auto next_stream = [&](Cursor& x) {
+        x.b = x.nb - 1;
+        advance(x);
+    };
+    // kCoopWaves units on: within the stream when it is long enough (the common case)
+    auto advance_coop = [&](Cursor& x) {
+        if (x.b + kCoopWaves < x.nb) {
+            x.b += kCoopWaves;
+            return;
+        }
+#pragma unroll
+        for (int i = 0; i < kCoopWaves; ++i) advance(x);
+    };
+
+    Loop L;
+    L.init_lane(lane);
+    typename Loop::State st;
+    // this wave's units: lo + k + kCoopWaves i, i < cnt
+    const long long cnt = lo + k < hi ? (hi - lo - k + kCoopWaves - 1) / kCoopWaves : 0;
+    long long issued = 0, done = 0;
+    Cursor ac = cur;
+    for (int i = 0; i < k; ++i) advance(ac);
+    Cursor cc = ac;
+    // the segment being accumulated: stream of sg, from unit su of the range
+    Cursor sg = cur;
+    long long su = lo;
+    bool have = false;  // this wave has folded a tile of the segment
+    const int cap = min(p.G, HT);
+    const size_t rec = (size_t)cap * (D + 2);
+
+    // close segment sg (every wave, in the same order), then move to the next stream
+    auto close = [&]() {
+        const long long sa = su - sg.b, send = min(hi, sa + sg.nb);
+        const bool whole = sg.b == 0 && sa + sg.nb <= hi;
+        const Heads hs = stream_heads<HT>(p, sg.c);
+        if (have) {
+            L.finish(st);
+            L.store_partial(st, slot[k], HT, hs.nh);
+        }
+        if (lane == 0) used[k] = have;
+        lds_barrier();
+        // wave k joins heads k HW .. k HW + HW - 1; a lane takes E head_dim elements
+        constexpr int HW = HT / kCoopWaves, LPH = 64 / HW, E = D / LPH;
+        const int h = k * HW + lane / LPH, d0 = (lane % LPH) * E;
+        if (h < hs.nh) {
+            float M = kNegInf;
+#pragma unroll
+            for (int j = 0; j < kCoopWaves; ++j)
+                if (used[j]) M = fmaxf(M, slot[j][HT * D + h]);
+            float Ls = 0.f, O[E];
+#pragma unroll
+            for (int e = 0; e < E; ++e) O[e] = 0.f;
+#pragma unroll
+            for (int j = 0; j < kCoopWaves; ++j) {
+                if (!used[j]) continue;
+                const float wt = fast_exp2(slot[j][HT * D + h] - M);
+                Ls += wt * slot[j][HT * D + HT + h];
+#pragma unroll
+                for (int e = 0; e < E; e += 4) {
+                    const f32x4 a = *(const f32x4*)&slot[j][h * D + d0 + e];
+                    O[e] += wt * a[0];
+                    O[e + 1] += wt * a[1];
+                    O[e + 2] += wt * a[2];
+                    O[e + 3] += wt * a[3];
+                }
+            }
+            if (whole) {
+                const float inv = Ls > 0.f ? 1.f / Ls : 0.f;
+                uint16_t* o = (uint16_t*)p.out + (row_of_uniform(p, sg.s) * p.Hq + hs.head0 + h) * D + d0;
+#pragma unroll
+                for (int e = 0; e < E; e += 4)
+                    *(uint2*)(o + e) = pack4<Loop::kKind>(O[e] * inv, O[e + 1] * inv, O[e + 2] * inv, O[e + 3] * inv);
+            } else {
+                // slot 0: the range's first segment; slot 1: its last, when that is another
+                float* r = p.ws + ((size_t)w * 2 + (su == lo ? 0 : 1)) * rec;
+#pragma unroll
+                for (int e = 0; e < E; e += 4) *(f32x4*)(r + h * D + d0 + e) = f32x4{O[e], O[e + 1], O[e + 2], O[e + 3]};
+                if (lane % LPH == 0) {
+                    r[cap * D + h] = M;
+                    r[cap * D + cap + h] = Ls;
+                }
+            }
+        }
+        lds_barrier();  // the slots are rewritten by the next segment
+        su = send;
+        next_stream(sg);
+        have = false;
+    };
+
+    auto issue = [&](typename Loop::Tile& t) {
+        const bool live = issued < cnt;
+        L.load(t, p.kc, p.vc, tile_src<Loop::kBS>(p, ac.s, ac.b, ac.c / p.chunks, ac.ctx, live));
+        if (live) {
+            advance_coop(ac);
+            ++issued;
+        }
+    };
+    // Issue tile `tn`, then fold tile `tc` (unit cc): first close the segments before
+    // cc's stream; when tc opens this wave's part of a segment its queries are loaded
+    // before tn's tiles and waited for right there, with tn's loads left in flight.
+    auto step = [&](typename Loop::Tile& tn, typename Loop::Tile& tc) {
+        while (sg.s != cc.s || sg.c != cc.c) close();
+        if (!have) {
+            const Heads hd = stream_heads<HT>(p, cc.c);
+            L.start(st, p.q, row_of_uniform(p, uniform(cc.s)), p.Hq, hd.head0, hd.nh);
+            have = true;
+            issue(tn);
+            vm_wait_le<Loop::kTileLoads>();
+        } else {
+            issue(tn);
+        }
+        L.block(st, tc, cc.ctx - cc.b * kTileTokens, p.scale_log2);
+        advance_coop(cc);
+        ++done;
+    };
+
+    // ring of R tiles: R - 1 blocks in flight while one is folded
+    typename Loop::Tile ring[R];
+#pragma unroll
+    for (int j = 0; j + 1 < R; ++j) issue(ring[j]);
+    while (done < cnt) {
+#pragma unroll
+        for (int j = 0; j < R; ++j) {
+            step(ring[(j + R - 1) % R], ring[j]);
+            if (done >= cnt) break;
+        }
+    }
+    while (su < hi) close();
 }
 
 // ---------------------------------------------------------------------------------------
@@ -796,10 +1006,17 @@ hipError_t run(const DecodeParams& p0, bool split, bool shallow, int slot, hipSt
             hipLaunchKernelGGL((decode_split_prologue<Loop::kElemBytes>), dim3(1), dim3(kPrologueThreads), 0, st, p,
                                NS);
         if (!shallow) {
-            // deep-ring loops are built for one wave per SIMD; the others take what fits
-            waves = resident_waves((const void*)decode_split<Loop, Loop::kRing>, slot * 2 + 1,
-                                   split_per_simd<Loop>());
-            hipLaunchKernelGGL((decode_split<Loop, Loop::kRing>), dim3(waves), dim3(64), 0, st, p);
+            if constexpr (Loop::kCoop) {
+                // one cooperative workgroup (a wave per SIMD) per compute unit
+                waves = (int)std::min<long long>(device_compute_units(), kMaxSplitWaves);
+                hipLaunchKernelGGL((decode_split_coop<Loop, Loop::kRing>), dim3(waves), dim3(64 * kCoopWaves), 0,
+                                   st, p);
+            } else {
+                // deep-ring loops are built for one wave per SIMD; the others take what fits
+                waves = resident_waves((const void*)decode_split<Loop, Loop::kRing>, slot * 2 + 1,
+                                       split_per_simd<Loop>());
+                hipLaunchKernelGGL((decode_split<Loop, Loop::kRing>), dim3(waves), dim3(64), 0, st, p);
+            }
         } else {
             waves = resident_waves((const void*)decode_split<Loop, 2>, slot * 2, 4);
             hipLaunchKernelGGL((decode_split<Loop, 2>), dim3(waves), dim3(64), 0, st, p);
