@@ -16,8 +16,12 @@
 // instructions on the way), two steps ahead, in a ring of three LDS stages, and
 // every wave folds the step into its rows with an online softmax:
 //   S^T = K Q^T        16x16x32 matrix cores, 16 keys x 16 rows per product
-//   O^T += V^T P^T     16x16x32 matrix cores over all 32 keys of the step, P split
-//                      into high and low 16-bit parts so that it keeps fp32 accuracy
+//   O^T += V^T P^T     16x16x32 matrix cores over all 32 keys of the step, P rounded
+//                      to the element type (bf16 or f16) as the product's operand, and
+//                      the softmax sum taken over the rounded weights: every output row
+//                      is then a convex combination of V rows whose weights are within
+//                      one rounding of the exact ones (a context of one token gives its
+//                      V row exactly)
 // The two score products of a step take the keys in the order that makes each
 // lane's eight probabilities the eight consecutive keys of one 16-byte V chunk:
 // product h (0, 1) has key 8 (i / 4) + 4 h + i % 4 as its row i, so lane group g
@@ -287,20 +291,13 @@ __device__ __forceinline__ void chunked_tile(const ChunkedParams& p, int idx, ch
             float pr[8];
 #pragma unroll
             for (int j = 0; j < 8; ++j) pr[j] = fast_exp2(__builtin_fmaf(s[j], c, off));
-            l[ht] += ((pr[0] + pr[1]) + (pr[2] + pr[3])) + ((pr[4] + pr[5]) + (pr[6] + pr[7]));
             const uint2 h0 = pack4<K>(pr[0], pr[1], pr[2], pr[3]);
             const uint2 h1 = pack4<K>(pr[4], pr[5], pr[6], pr[7]);
-            const uint2 l0 = pack4<K>(pr[0] - lo16<K>(h0.x), pr[1] - hi16<K>(h0.x), pr[2] - lo16<K>(h0.y),
-                                      pr[3] - hi16<K>(h0.y));
-            const uint2 l1 = pack4<K>(pr[4] - lo16<K>(h1.x), pr[5] - hi16<K>(h1.x), pr[6] - lo16<K>(h1.y),
-                                      pr[7] - hi16<K>(h1.y));
-            const uint4 phi = make_uint4(h0.x, h0.y, h1.x, h1.y);
-            const uint4 plo = make_uint4(l0.x, l0.y, l1.x, l1.y);
-            // high parts, then the remainders: an accumulator is reused DT products later
+            l[ht] += ((lo16<K>(h0.x) + hi16<K>(h0.x)) + (lo16<K>(h0.y) + hi16<K>(h0.y))) +
+                     ((lo16<K>(h1.x) + hi16<K>(h1.x)) + (lo16<K>(h1.y) + hi16<K>(h1.y)));
+            const uint4 pw = make_uint4(h0.x, h0.y, h1.x, h1.y);
 #pragma unroll
-            for (int dt = 0; dt < DT; ++dt) acc[ht][dt] = mma_16x16x32<K>(vf[dt], phi, acc[ht][dt]);
-#pragma unroll
-            for (int dt = 0; dt < DT; ++dt) acc[ht][dt] = mma_16x16x32<K>(vf[dt], plo, acc[ht][dt]);
+            for (int dt = 0; dt < DT; ++dt) acc[ht][dt] = mma_16x16x32<K>(vf[dt], pw, acc[ht][dt]);
         }
     };
 

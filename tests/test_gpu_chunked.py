@@ -8,7 +8,7 @@ import oracle
 import paged_kv_cache_265_amd as pkv
 from workloads.gen import make_chunked_case
 
-from helpers import bits, check_close, dev
+from helpers import bits, check_close, dev, vmax_of
 
 pytestmark = pytest.mark.gpu
 
@@ -55,7 +55,7 @@ def test_chunked_matches_oracle(dtype, G, Hkv, D, cached, q_lens):
     case = make_chunked_case([31, G, D], dtype, cached, q_lens, G * Hkv, Hkv, D, label="random")
     ref, pool = oracle_chunked(case)
     out, kc, vc = run_chunked(case)
-    check_close(out, ref, dtype, f"chunked {dtype} G={G}")
+    check_close(out, ref, dtype, f"chunked {dtype} G={G}", weights_vmax=vmax_of(case.paged.logical_v))
     # the chunk's K/V went into the pool bit for bit
     assert torch.equal(bits(kc.cpu()), bits(pool.key_cache))
     assert torch.equal(bits(vc.cpu()), bits(pool.value_cache))
@@ -70,7 +70,7 @@ def test_chunk_of_one_row_equals_decode():
                                dev(case.paged.context_lens), case.scale)
     torch.cuda.synchronize()
     ref, _ = oracle_chunked(case)
-    check_close(out, ref, "bf16", "L=1 chunked")
+    check_close(out, ref, "bf16", "L=1 chunked", weights_vmax=vmax_of(case.paged.logical_v))
     check_close(dec, ref, "bf16", "L=1 decode")
 
 

@@ -14,7 +14,7 @@ import oracle
 import paged_kv_cache_265_amd as pkv
 from workloads.gen import make_chunked_case, reblock
 
-from helpers import bits, check_close, dev
+from helpers import bits, check_close, dev, vmax_of
 
 pytestmark = pytest.mark.gpu
 
@@ -88,7 +88,7 @@ def test_mixed_matches_oracle_and_the_separate_calls(dtype, G, Hkv, D, cached, q
     case = make_chunked_case([71, G, D, len(q_lens)], dtype, cached, q_lens, G * Hkv, Hkv, D)
     ref = oracle_rows(case)
     out = run(case, pkv.paged_attention_mixed)
-    check_close(out, ref, dtype, f"mixed {dtype} G={G}")
+    check_close(out, ref, dtype, f"mixed {dtype} G={G}", weights_vmax=vmax_of(case.paged.logical_v))
     sep = run(case, pkv.paged_attention_chunked)
     rows = decode_rows(case)
     pre = np.setdiff1d(np.arange(out.shape[0]), rows)
@@ -113,7 +113,7 @@ def test_mixed_block_sizes(bs):
     p = reblock(case.paged, bs, np.random.default_rng(bs))
     ref = oracle_rows(case, p)
     out = run(case, pkv.paged_attention_mixed, p)
-    check_close(out, ref, "bf16", f"mixed bs={bs}")
+    check_close(out, ref, "bf16", f"mixed bs={bs}", weights_vmax=vmax_of(p.logical_v))
     # block size changes nothing: same bits as at 16
     out16 = run(case, pkv.paged_attention_mixed)
     assert torch.equal(bits(out), bits(out16))
@@ -132,4 +132,4 @@ def test_mixed_nan_slots_never_leak():
     assert torch.isnan(case.paged.pool.key_cache).any()
     out = run(case, pkv.paged_attention_mixed)
     assert torch.isfinite(out).all()
-    check_close(out, oracle_rows(case), "bf16", "nan slots")
+    check_close(out, oracle_rows(case), "bf16", "nan slots", weights_vmax=vmax_of(case.paged.logical_v))
