@@ -202,15 +202,19 @@ __device__ __forceinline__ void chunked_tile(const ChunkedParams& p, int idx, ch
             qv[ht][ks] = live ? *(const uint4*)(qp + ((size_t)(qb0 + tok) * p.Hq + kvh * G + j) * D + (gq + 4 * ks) * 8)
                               : make_uint4(0, 0, 0, 0);
     }
-    float m[NH], l[NH];
-    f32x4 acc[NH][DT];
+    // the softmax sums come out of the matrix cores: a head_dim tile of ones beside V,
+    // so that every element of lsum[ht] is the row's sum of its rounded weights
+    float m[NH];
+    f32x4 acc[NH][DT], lsum[NH];
 #pragma unroll
     for (int ht = 0; ht < NH; ++ht) {
         m[ht] = kNegInf;
-        l[ht] = 0.f;
+        lsum[ht] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int dt = 0; dt < DT; ++dt) acc[ht][dt] = f32x4{0.f, 0.f, 0.f, 0.f};
     }
+    const uint32_t one2 = pack4<K>(1.f, 1.f, 1.f, 1.f).x;  // two 16-bit ones
+    const uint4 ones = make_uint4(one2, one2, one2, one2);
 
     // ---- one step: 32 keys into this wave's 32 rows ----------------------------------
     auto fold = [&](int step, const char* stage) {
@@ -282,7 +286,7 @@ __device__ __forceinline__ void chunked_tile(const ChunkedParams& p, int idx, ch
             if (__ballot(lm > m[ht] + kRescaleSlack)) {
                 const float mn = fmaxf(m[ht], xor_max(xor_max(lm, 16), 32));
                 const float alpha = fast_exp2(m[ht] - mn);
-                l[ht] *= alpha;
+                lsum[ht] *= alpha;
 #pragma unroll
                 for (int dt = 0; dt < DT; ++dt) acc[ht][dt] *= alpha;
                 m[ht] = mn;
@@ -293,11 +297,10 @@ __device__ __forceinline__ void chunked_tile(const ChunkedParams& p, int idx, ch
             for (int j = 0; j < 8; ++j) pr[j] = fast_exp2(__builtin_fmaf(s[j], c, off));
             const uint2 h0 = pack4<K>(pr[0], pr[1], pr[2], pr[3]);
             const uint2 h1 = pack4<K>(pr[4], pr[5], pr[6], pr[7]);
-            l[ht] += ((lo16<K>(h0.x) + hi16<K>(h0.x)) + (lo16<K>(h0.y) + hi16<K>(h0.y))) +
-                     ((lo16<K>(h1.x) + hi16<K>(h1.x)) + (lo16<K>(h1.y) + hi16<K>(h1.y)));
             const uint4 pw = make_uint4(h0.x, h0.y, h1.x, h1.y);
 #pragma unroll
             for (int dt = 0; dt < DT; ++dt) acc[ht][dt] = mma_16x16x32<K>(vf[dt], pw, acc[ht][dt]);
+            lsum[ht] = mma_16x16x32<K>(ones, pw, lsum[ht]);
         }
     };
 
@@ -331,12 +334,12 @@ __device__ __forceinline__ void chunked_tile(const ChunkedParams& p, int idx, ch
 
 #pragma unroll
     for (int ht = 0; ht < NH; ++ht) {
-        l[ht] = xor_sum(xor_sum(l[ht], 16), 32);
         const int r = row0 + ht * 16 + col;
         if (r >= nrows) continue;
         const int tok = r / G;
         const int j = r - tok * G;
-        const float inv = 1.f / l[ht];
+        mfma_result_fence();
+        const float inv = 1.f / lsum[ht][0];
         char* orow = (char*)p.out + ((size_t)(qb0 + tok) * p.Hq + kvh * G + j) * D * 2;
 #pragma unroll
         for (int dt = 0; dt < DT; ++dt) {
