@@ -280,8 +280,11 @@ __device__ __forceinline__ void chunked_tile(const ChunkedParams& p, int idx, ch
             // this lane's maximum of its eight scaled scores (the scale is positive); only
             // when one exceeds the reference by the slack is the row maximum over the
             // four lanes of the row needed
-            const float lm =
-                fmaxf(fmaxf(fmaxf(s[0], s[1]), fmaxf(s[2], s[3])), fmaxf(fmaxf(s[4], s[5]), fmaxf(s[6], s[7]))) * c;
+            // (IEEE maximum: no NaN can be among the scores here -- slots past the context are
+            // masked above -- so it needs none of the operand quieting fmaxf costs)
+            const float lm = max_nonan(max_nonan(max_nonan(s[0], s[1]), max_nonan(s[2], s[3])),
+                                       max_nonan(max_nonan(s[4], s[5]), max_nonan(s[6], s[7]))) *
+                             c;
             // key 0 is visible to every row, so m is finite from the first step on
             if (__ballot(lm > m[ht] + kRescaleSlack)) {
                 const float mn = fmaxf(m[ht], xor_max(xor_max(lm, 16), 32));

@@ -188,6 +188,10 @@ __device__ __forceinline__ bool contract_broken(const unsigned long long* guard)
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
+// IEEE 754-2019 maximum (v_maximum3_f32 on gfx950): for operands that are never NaN it
+// equals fmaxf, without the operand quieting fmaxf needs in IEEE mode
+__device__ __forceinline__ float max_nonan(float a, float b) { return __builtin_elementwise_maximum(a, b); }
+
 __device__ __forceinline__ int lane_id() { return (int)(threadIdx.x & 63); }
 
 // Assert that v is the same in every lane, so that addresses built from it stay in
