@@ -140,7 +140,7 @@ __device__ __forceinline__ void chunked_tile(const ChunkedParams& p, int idx, ch
         const int rows_per_load = 64 / Lds::KCH;
         const int r = jj * rows_per_load + lane / Lds::KCH;  // key row in the step
         const int c = Lds::kpos(r, lane % Lds::KCH);        // the chunk this slot holds
-        kblk[j] = r / BS;
+        kblk[j] = uniform(r / BS);  // the load's four rows lie in one block
         koff[j] = (uint32_t)((r % BS) * D * 2 + c * 16);
     }
 #pragma unroll
@@ -149,7 +149,7 @@ __device__ __forceinline__ void chunked_tile(const ChunkedParams& p, int idx, ch
         const int slot = jj * 64 + lane;  // [half][chunk][d]
         const int d = slot % D, hc = slot / D;
         const int key = 8 * hc;           // first key of the chunk within the step
-        vblk[j] = key / BS;
+        vblk[j] = uniform(key / BS);  // the 64 lanes share one chunk
         voff[j] = (uint32_t)(d * BS * 2 + (key % BS) * 2);
     }
     auto issue = [&](int step, char* stage) {
@@ -170,7 +170,7 @@ __device__ __forceinline__ void chunked_tile(const ChunkedParams& p, int idx, ch
             rsrc_t r = kr[0];
 #pragma unroll
             for (int b = 1; b < NBS; ++b)
-                if (uniform(kblk[j]) == b) r = kr[b];
+                if (kblk[j] == b) r = kr[b];
             load_to_lds<kNonTemporal>(r, kl + (w * Lds::KLOADS_W + j) * 1024, koff[j]);
         }
         // V chunks are 16 of the 32 bytes of a head_dim row (block size 16 or 32): the
@@ -180,7 +180,7 @@ __device__ __forceinline__ void chunked_tile(const ChunkedParams& p, int idx, ch
             rsrc_t r = vr[0];
 #pragma unroll
             for (int b = 1; b < NBS; ++b)
-                if (uniform(vblk[j]) == b) r = vr[b];
+                if (vblk[j] == b) r = vr[b];
             load_to_lds<BS == 8 ? kNonTemporal : 0>(r, vl + (w * Lds::VLOADS_W + j) * 1024, voff[j]);
         }
     };
