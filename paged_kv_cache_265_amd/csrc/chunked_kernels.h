@@ -61,6 +61,30 @@ struct ChunkLds {
     static constexpr int KLOADS = KBYTES / 1024, VLOADS = VBYTES / 1024;
     static constexpr int KLOADS_W = KLOADS / NW, VLOADS_W = VLOADS / NW;
     static_assert(KLOADS % NW == 0 && VLOADS % NW == 0, "every wave moves the same share");
+    // key row of lane `lane` in K load j of wave w, and the first key of the 8-key
+    // chunk of V load j of wave w
+    static constexpr __host__ __device__ int k_row(int w, int j, int lane) {
+        return (w * KLOADS_W + j) * (64 / KCH) + lane / KCH;
+    }
+    static constexpr __host__ __device__ int v_key(int w, int j, int lane) {
+        return 8 * (((w * VLOADS_W + j) * 64 + lane) / D);
+    }
+    static constexpr __host__ __device__ int block_of_wave(int w, int bs) { return k_row(w, 0, 0) / bs; }
+    // every load of a wave, K and V, lies in the wave's one block
+    static constexpr bool one_block_per_wave(int bs) {
+        for (int w = 0; w < NW; ++w)
+            for (int lane = 0; lane < 64; ++lane) {
+                for (int j = 0; j < KLOADS_W; ++j)
+                    if (k_row(w, j, lane) / bs != block_of_wave(w, bs)) return false;
+                for (int j = 0; j < VLOADS_W; ++j)
+                    if (v_key(w, j, lane) / bs != block_of_wave(w, bs) || (v_key(w, j, lane) + 7) / bs !=
+                                                                             block_of_wave(w, bs))
+                        return false;
+            }
+        return true;
+    }
+    static_assert(one_block_per_wave(8) && one_block_per_wave(16) && one_block_per_wave(32),
+                  "each wave's loads of a step come from one pool block");
     // position of chunk c of key row r
     static __device__ __forceinline__ int kpos(int r, int c) {
         if constexpr (D == 128)
@@ -129,60 +153,43 @@ __device__ __forceinline__ void chunked_tile(const ChunkedParams& p, int idx, ch
     // access), so every step issues the same loads and the wait before a fold counts
     // exactly: KLOADS_W + VLOADS_W per wave and step.
     const int32_t* table = p.block_tables + (size_t)seg * p.MB;
-    // this lane's part of each of the wave's loads: K load j covers key rows 4 j'..+3
-    // (j' = the workgroup-wide load index), V load j covers 64 head_dim rows of one
-    // (half, chunk)
+    // this lane's part of each of the wave's loads: K load j covers key rows
+    // rows_per_load j'..+rows_per_load-1 (j' = the workgroup-wide load index), V load j
+    // covers 64 head_dim rows of one (half, chunk).  Every load of wave w lies in one
+    // pool block of the step, block_of_wave(w) (checked at compile time below), so a
+    // wave reads one table entry and builds one K and one V resource per step.
+    const int myblk = uniform(ChunkLds<D>::block_of_wave(w, BS));
     uint32_t koff[Lds::KLOADS_W], voff[Lds::VLOADS_W];
-    int kblk[Lds::KLOADS_W], vblk[Lds::VLOADS_W];
 #pragma unroll
     for (int j = 0; j < Lds::KLOADS_W; ++j) {
-        const int jj = w * Lds::KLOADS_W + j;
-        const int rows_per_load = 64 / Lds::KCH;
-        const int r = jj * rows_per_load + lane / Lds::KCH;  // key row in the step
-        const int c = Lds::kpos(r, lane % Lds::KCH);        // the chunk this slot holds
-        kblk[j] = uniform(r / BS);  // the load's four rows lie in one block
+        const int r = Lds::k_row(w, j, lane);           // key row in the step
+        const int c = Lds::kpos(r, lane % Lds::KCH);  // the chunk this slot holds
         koff[j] = (uint32_t)((r % BS) * D * 2 + c * 16);
     }
 #pragma unroll
     for (int j = 0; j < Lds::VLOADS_W; ++j) {
-        const int jj = w * Lds::VLOADS_W + j;
-        const int slot = jj * 64 + lane;  // [half][chunk][d]
-        const int d = slot % D, hc = slot / D;
-        const int key = 8 * hc;           // first key of the chunk within the step
-        vblk[j] = uniform(key / BS);  // the 64 lanes share one chunk
+        const int slot = (w * Lds::VLOADS_W + j) * 64 + lane;  // [half][chunk][d]
+        const int d = slot % D;
+        const int key = Lds::v_key(w, j, lane);  // first key of the chunk within the step
         voff[j] = (uint32_t)(d * BS * 2 + (key % BS) * 2);
     }
     auto issue = [&](int step, char* stage) {
         char* kl = stage;
         char* vl = kl + Lds::KBYTES;
-        const int b0 = step * NBS;
-        rsrc_t kr[NBS], vr[NBS];
+        const int b = step * NBS + myblk;
+        const bool live = b < nblk;
+        const int ph = live ? scalar_load(table, (size_t)uniform(b)) : 0;
+        const size_t t = ((size_t)ph * p.Hkv + kvh) * kTile;
+        const rsrc_t kr = tile_rsrc((const char*)p.kc + t, live ? kTile : 0);
+        const rsrc_t vr = tile_rsrc((const char*)p.vc + t, live ? kTile : 0);
 #pragma unroll
-        for (int b = 0; b < NBS; ++b) {
-            const bool live = b0 + b < nblk;
-            const int ph = live ? scalar_load(table, (size_t)uniform(b0 + b)) : 0;
-            const size_t t = ((size_t)ph * p.Hkv + kvh) * kTile;
-            kr[b] = tile_rsrc((const char*)p.kc + t, live ? kTile : 0);
-            vr[b] = tile_rsrc((const char*)p.vc + t, live ? kTile : 0);
-        }
-#pragma unroll
-        for (int j = 0; j < Lds::KLOADS_W; ++j) {
-            rsrc_t r = kr[0];
-#pragma unroll
-            for (int b = 1; b < NBS; ++b)
-                if (kblk[j] == b) r = kr[b];
-            load_to_lds<kNonTemporal>(r, kl + (w * Lds::KLOADS_W + j) * 1024, koff[j]);
-        }
+        for (int j = 0; j < Lds::KLOADS_W; ++j)
+            load_to_lds<kNonTemporal>(kr, kl + (w * Lds::KLOADS_W + j) * 1024, koff[j]);
         // V chunks are 16 of the 32 bytes of a head_dim row (block size 16 or 32): the
         // other half is read by the neighbouring load, so V keeps the default policy
 #pragma unroll
-        for (int j = 0; j < Lds::VLOADS_W; ++j) {
-            rsrc_t r = vr[0];
-#pragma unroll
-            for (int b = 1; b < NBS; ++b)
-                if (vblk[j] == b) r = vr[b];
-            load_to_lds<BS == 8 ? kNonTemporal : 0>(r, vl + (w * Lds::VLOADS_W + j) * 1024, voff[j]);
-        }
+        for (int j = 0; j < Lds::VLOADS_W; ++j)
+            load_to_lds<BS == 8 ? kNonTemporal : 0>(vr, vl + (w * Lds::VLOADS_W + j) * 1024, voff[j]);
     };
 
     // ---- this lane's rows: Q as the B operand of the score product; dead rows see
