@@ -156,33 +156,6 @@ int paged_attention_decode(void* out, const void* query, const void* key_cache, 
                            size_t workspace_bytes, void* stream);
 
 /*
- * paged_attention_decode_append -- one decode step: the write of every sequence's
- * newest token and the attention over the cache that holds it ([P3] section 3.1: a
- * decode step appends the new token's K/V and attends over them; [P2] section 1.6).
- *
- * Equal, output and caches bit for bit, to reshape_and_cache of new_key / new_value at
- * each sequence's newest position followed by paged_attention_decode with the same
- * arguments:
- *   new_key, new_value: device [num_seqs][num_kv_heads][head_dim] of the cache's
- *     element type, 16-byte aligned: the K and V of token context_lens[s] - 1 of
- *     sequence s (context_lens counts it), written to its slot
- *     block_tables[s][(n-1) / BS] * BS + (n-1) % BS; sequences with n = 0 write
- *     nothing.
- *   key_cache, value_cache: written (the newest tokens' slots only) and read.
- * The balanced split writes the tokens from inside the decode launch (the wave that
- * reads a sequence's last tile writes its newest token first); fixed partitions, and
- * kv heads whose query heads are split into several chunks, write them with a small
- * kernel before the decode launch.  Same workspace (pkv_decode_workspace_size of the
- * same arguments) and conventions as paged_attention_decode.
- */
-int paged_attention_decode_append(void* out, const void* query, const void* new_key, const void* new_value,
-                                  void* key_cache, void* value_cache, const int32_t* block_tables,
-                                  const int32_t* context_lens, int num_seqs, int num_q_heads, int num_kv_heads,
-                                  int head_dim, int block_size, int num_blocks, int max_blocks_per_seq, float scale,
-                                  int dtype, int partition_size, void* workspace, size_t workspace_bytes,
-                                  void* stream);
-
-/*
  * paged_attention_decode_static -- paged_attention_decode without a workspace
  * argument, for callers that cannot allocate device memory: code under HIP graph
  * capture, serving loops that must not call the allocator, harnesses that forbid it.

@@ -207,8 +207,7 @@ int decode_call(const char* fn, void* out, const void* query, const void* key_ca
                 const int32_t* block_tables, const int32_t* context_lens, int num_seqs, int num_q_heads,
                 int num_kv_heads, int head_dim, int block_size, int num_blocks, int max_blocks_per_seq, float scale,
                 int dtype, int partition_size, void* workspace, size_t workspace_bytes, bool use_static, int path,
-                int ring, void* stream, const void* new_key = nullptr, const void* new_value = nullptr,
-                bool append = false) {
+                int ring, void* stream) {
     int rc;
     if ((rc = check_pool(fn, num_kv_heads, head_dim, block_size, num_blocks, dtype)) != PKV_OK) return rc;
     if ((rc = check_heads(fn, num_q_heads, num_kv_heads)) != PKV_OK) return rc;
@@ -225,12 +224,10 @@ int decode_call(const char* fn, void* out, const void* query, const void* key_ca
     if (path == 2 && dtype == PKV_F32)
         return set_error(PKV_ERR_UNSUPPORTED, "%s: the matrix-core path takes 16-bit types only", fn);
     if (num_seqs == 0) return PKV_OK;
-    if (!out || !query || !key_cache || !value_cache || !block_tables || !context_lens ||
-        (append && (!new_key || !new_value)))
+    if (!out || !query || !key_cache || !value_cache || !block_tables || !context_lens)
         return set_error(PKV_ERR_INVALID, "%s: null pointer argument", fn);
     if (!aligned(out, 16) || !aligned(query, 16) || !aligned(key_cache, 16) || !aligned(value_cache, 16) ||
-        !aligned(block_tables, 4) || !aligned(context_lens, 4) ||
-        (append && (!aligned(new_key, 16) || !aligned(new_value, 16))))
+        !aligned(block_tables, 4) || !aligned(context_lens, 4))
         return set_error(PKV_ERR_INVALID, "%s: misaligned pointer (16 bytes for tensors, 4 for int32 arrays)", fn);
     const int mp = partition_size > 0 ? max_parts(max_blocks_per_seq, block_size, partition_size) : 0;
     const int G = num_q_heads / num_kv_heads;
@@ -272,8 +269,6 @@ int decode_call(const char* fn, void* out, const void* query, const void* key_ca
     p.block_tables = block_tables;
     p.context_lens = context_lens;
     p.cu_q = nullptr;
-    p.new_k = append ? new_key : nullptr;
-    p.new_v = append ? new_value : nullptr;
     if (partition_size == 0) {
         p.starts = (long long*)workspace;
         p.notes = (pkv::MergeNote*)((char*)workspace + split_starts_bytes(num_seqs));
@@ -312,18 +307,6 @@ int paged_attention_decode(void* out, const void* query, const void* key_cache, 
     return decode_call("paged_attention_decode", out, query, key_cache, value_cache, block_tables, context_lens,
                        num_seqs, num_q_heads, num_kv_heads, head_dim, block_size, num_blocks, max_blocks_per_seq,
                        scale, dtype, partition_size, workspace, workspace_bytes, false, 0, 0, stream);
-}
-
-int paged_attention_decode_append(void* out, const void* query, const void* new_key, const void* new_value,
-                                  void* key_cache, void* value_cache, const int32_t* block_tables,
-                                  const int32_t* context_lens, int num_seqs, int num_q_heads, int num_kv_heads,
-                                  int head_dim, int block_size, int num_blocks, int max_blocks_per_seq, float scale,
-                                  int dtype, int partition_size, void* workspace, size_t workspace_bytes,
-                                  void* stream) {
-    return decode_call("paged_attention_decode_append", out, query, key_cache, value_cache, block_tables,
-                       context_lens, num_seqs, num_q_heads, num_kv_heads, head_dim, block_size, num_blocks,
-                       max_blocks_per_seq, scale, dtype, partition_size, workspace, workspace_bytes, false, 0, 0,
-                       stream, new_key, new_value, true);
 }
 
 int pkv_decode_variant(void* out, const void* query, const void* key_cache, const void* value_cache,
@@ -491,7 +474,6 @@ int paged_attention_mixed(void* out, const void* query, const int32_t* cu_q_lens
     d.block_tables = block_tables;
     d.context_lens = context_lens;
     d.cu_q = cu_q_lens;
-    d.new_k = d.new_v = nullptr;
     d.starts = (long long*)workspace;
     d.notes = (pkv::MergeNote*)((char*)workspace + split_starts_bytes(num_segs));
     d.ws = (float*)((char*)workspace + split_prefix_bytes(num_segs, mixed_decode_waves()));

@@ -228,63 +228,6 @@ __device__ __forceinline__ Cursor uniform_cursor(const Cursor& x) {
     return Cursor{uniform(x.s), uniform(x.c), uniform(x.b), uniform(x.nb), uniform(x.ctx)};
 }
 
-// Decode with append: one wave writes the newest token of sequence s (position
-// ctx - 1, ctx >= 1) for kv head kvh from new_k / new_v [S][Hkv][D] into its slot of
-// the pool, found through the block table: the K row (token-major tile) and the V
-// column (head_dim-major tile).  Plain stores: the same wave reads the tile later.
-template <int EB>
-__device__ __forceinline__ void append_newest(const DecodeParams& p, int s, int kvh, int ctx, int lane) {
-    const int t = ctx - 1;
-    const long long blk = scalar_load(p.block_tables + (size_t)s * p.MB, (size_t)uniform(t / p.BS));
-    const int off = t % p.BS;
-    const size_t tile = (size_t)blk * p.Hkv + kvh;
-    const size_t src = ((size_t)s * p.Hkv + kvh) * p.D * EB;
-    const char* nk = (const char*)p.new_k + src;
-    const char* nv = (const char*)p.new_v + src;
-    char* kd = (char*)p.kc + (tile * p.BS + off) * p.D * EB;
-    for (int i = lane * 4; i < p.D * EB; i += 256) *(uint32_t*)(kd + i) = *(const uint32_t*)(nk + i);
-    char* vd = (char*)p.vc + (tile * p.D * p.BS + off) * EB;
-    for (int d = lane; d < p.D; d += 64) {
-        if constexpr (EB == 4)
-            *(uint32_t*)(vd + (size_t)d * p.BS * EB) = *(const uint32_t*)(nv + d * EB);
-        else
-            *(uint16_t*)(vd + (size_t)d * p.BS * EB) = *(const uint16_t*)(nv + d * EB);
-    }
-}
-
-// The appends of a piece of the balanced split: every stream whose last tile lies in
-// [lo, hi) (starting from cursor cur at unit lo) gets its sequence's newest token
-// written by the wave that folds that tile -- wave `k` of `nw` waves that fold every
-// nw-th unit from lo -- before the wave loads any tile.  Only for streams that are the
-// one stream of their kv head (chunks == 1): no other wave reads the tile.
-template <int EB>
-__device__ __forceinline__ void append_in_range(const DecodeParams& p, Cursor x, long long lo, long long hi, int k,
-                                                int nw, int lane) {
-    long long u = lo;  // the unit x points at
-    bool wrote = false;
-    while (true) {
-        const long long last = u - x.b + x.nb - 1;  // the stream's last unit
-        if (last >= hi) break;
-        if ((int)((last - lo) % nw) == k) {
-            append_newest<EB>(p, x.s, x.c, x.ctx, lane);
-            wrote = true;
-        }
-        u = last + 1;
-        if (u >= hi) break;
-        // next stream: first tile of stream c + 1, or of the next sequence with tiles
-        x.b = 0;
-        if (++x.c == p.Hkv * p.chunks) {
-            x.c = 0;
-            do {
-                ++x.s;
-                x.ctx = dec_ctx_uniform(p, uniform(x.s));
-                x.nb = ntiles(x.ctx);
-            } while (x.nb == 0);
-        }
-    }
-    if (wrote) vm_wait_le<0>();  // the stores are done before the tile loads go out
-}
-
 // Range [lo, hi) of the U units taken by split piece w of the N launched (a wave, or
 // a cooperative workgroup), Nw = working_waves(U, N): [w U / Nw, (w+1) U / Nw), empty
 // for w >= Nw; cur locates unit lo.  With `writer` (one wave per piece) also the
@@ -388,7 +331,6 @@ __device__ __forceinline__ void decode_split_wave(const DecodeParams& p, long lo
     lo = uniform(lo);
     hi = uniform(hi);
     cur = uniform_cursor(cur);
-    if (p.new_k) append_in_range<Loop::kElemBytes>(p, cur, lo, hi, 0, 1, lane);
     auto advance = [&](Cursor& x) {
         if (++x.b < x.nb) return;
         x.b = 0;
@@ -512,7 +454,6 @@ __global__ __launch_bounds__(64 * kCoopWaves, 1) void decode_split_coop(DecodePa
     lo = uniform(lo);
     hi = uniform(hi);
     cur = uniform_cursor(cur);
-    if (p.new_k) append_in_range<Loop::kElemBytes>(p, cur, lo, hi, k, kCoopWaves, lane);
     auto advance = [&](Cursor& x) {
         if (++x.b < x.nb) return;
         x.b = 0;
@@ -652,21 +593,6 @@ __global__ __launch_bounds__(64 * kCoopWaves, 1) void decode_split_coop(DecodePa
         }
     }
     while (su < hi) close();
-}
-
-// ---------------------------------------------------------------------------------------
-// decode with append, where the decode kernels cannot write the newest tokens
-// themselves (fixed partitions; several query-head chunks reading one kv head's tile):
-// workgroup (s, kvh) writes sequence s's newest token of kv head kvh before the decode
-// launch
-// ---------------------------------------------------------------------------------------
-template <int EB>
-__global__ __launch_bounds__(64) void decode_append_newest(DecodeParams p) {
-    if (contract_broken(p.guard)) return;
-    const int s = blockIdx.x / p.Hkv, kvh = blockIdx.x - s * p.Hkv;
-    const int ctx = p.context_lens[s];
-    if (ctx <= 0) return;
-    append_newest<EB>(p, s, kvh, ctx, lane_id());
 }
 
 // ---------------------------------------------------------------------------------------
@@ -1075,12 +1001,6 @@ hipError_t run(const DecodeParams& p0, bool split, bool shallow, int slot, hipSt
     p.chunks = (p.G + Loop::HT - 1) / Loop::HT;
     const int NS = p.Hkv * p.chunks;
     int waves = 0;
-    if (p.new_k && (!split || p.chunks > 1)) {
-        // the decode kernels write the newest tokens only when one wave reads each tile
-        hipLaunchKernelGGL((decode_append_newest<Loop::kElemBytes>), dim3((unsigned)(p.S * p.Hkv)), dim3(64), 0, st,
-                           p);
-        p.new_k = p.new_v = nullptr;
-    }
     if (split) {
         if (p.S > kInWaveSeqs)
             hipLaunchKernelGGL((decode_split_prologue<Loop::kElemBytes>), dim3(1), dim3(kPrologueThreads), 0, st, p,

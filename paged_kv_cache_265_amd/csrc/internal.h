@@ -46,11 +46,6 @@ struct DecodeParams {
     // cu_q[s] .. cu_q[s+1]-1; only one-row segments are decode sequences, the others
     // get no units and no output here.
     const int32_t* cu_q;
-    // paged_attention_decode_append: the newest token's K and V of every sequence,
-    // [S][Hkv][D] (NULL otherwise), written to position context_lens[s] - 1 through the
-    // block table before any tile is read
-    const void* new_k;
-    const void* new_v;
     float* ws;        // partial records: acc[cap][D], m[cap], l[cap] (m in log2 units)
     long long* starts;  // balanced split: first unit of every sequence, then the unit count
     MergeNote* notes;      // balanced split: one per wave (see MergeNote)

@@ -35,7 +35,6 @@ SYMBOLS = (
     "pkv_decode_workspace_size",
     "paged_attention_decode",
     "paged_attention_decode_static",
-    "paged_attention_decode_append",
     "pkv_decode_variant",
     "pkv_decode_variant_workspace_size",
     "paged_attention_chunked",
@@ -83,8 +82,6 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.paged_attention_decode.restype = I
     lib.paged_attention_decode_static.argtypes = [P, P, P, P, P, P, I, I, I, I, I, I, I, F, I, I, P]
     lib.paged_attention_decode_static.restype = I
-    lib.paged_attention_decode_append.argtypes = [P, P, P, P, P, P, P, P, I, I, I, I, I, I, I, F, I, I, P, Z, P]
-    lib.paged_attention_decode_append.restype = I
     lib.pkv_decode_variant.argtypes = [P, P, P, P, P, P, I, I, I, I, I, I, I, F, I, I, P, Z, I, I, P]
     lib.pkv_decode_variant.restype = I
     lib.pkv_decode_variant_workspace_size.argtypes = [I] * 10
@@ -203,33 +200,6 @@ def paged_attention_decode(out: torch.Tensor, query: torch.Tensor, key_cache: to
     rc = load_library().paged_attention_decode(
         _ptr(out), _ptr(query), _ptr(key_cache), _ptr(value_cache), _ptr(block_tables), _ptr(context_lens), S, Hq,
         Hkv, D, BS, NB, MB, float(scale), dt, int(partition_size), _ptr(workspace), ws_bytes, _stream(stream))
-    _check(rc)
-    return out
-
-
-def paged_attention_decode_append(out: torch.Tensor, query: torch.Tensor, new_key: torch.Tensor,
-                                  new_value: torch.Tensor, key_cache: torch.Tensor, value_cache: torch.Tensor,
-                                  block_tables: torch.Tensor, context_lens: torch.Tensor, scale: float,
-                                  partition_size: int = 0, workspace: Optional[torch.Tensor] = None,
-                                  stream=None) -> torch.Tensor:
-    """One decode step: writes each sequence's newest token (new_key / new_value
-    [S, Hkv, D], position context_lens[s] - 1) into the cache and decodes, as
-    reshape_and_cache + paged_attention_decode would (see include/pkv.h)."""
-    _contig(out, query, new_key, new_value, key_cache, value_cache, block_tables, context_lens)
-    S, Hq, D = query.shape
-    NB, Hkv, BS, _ = key_cache.shape
-    MB = block_tables.shape[1] if block_tables.dim() == 2 else 0
-    dt = _dtype(out, query, new_key, new_value, key_cache, value_cache)
-    if tuple(new_key.shape) != (S, Hkv, D) or tuple(new_value.shape) != (S, Hkv, D):
-        raise ValueError(f"new_key / new_value must be [{S}, {Hkv}, {D}]")
-    need = decode_workspace_size(S, Hq, Hkv, D, BS, max(MB, 1), partition_size)
-    if workspace is None and need > 0:
-        workspace = torch.empty(need, dtype=torch.uint8, device=query.device)
-    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
-    rc = load_library().paged_attention_decode_append(
-        _ptr(out), _ptr(query), _ptr(new_key), _ptr(new_value), _ptr(key_cache), _ptr(value_cache),
-        _ptr(block_tables), _ptr(context_lens), S, Hq, Hkv, D, BS, NB, MB, float(scale), dt, int(partition_size),
-        _ptr(workspace), ws_bytes, _stream(stream))
     _check(rc)
     return out
 

@@ -170,34 +170,6 @@ def test_decode_static_rejects_a_need_beyond_the_static_scratch():
     assert _decode_static(num_seqs=0, out=None) == 0
 
 
-def _decode_append(**over):
-    a = dict(out=FAKE, query=FAKE, new_key=FAKE, new_value=FAKE, key_cache=FAKE, value_cache=FAKE,
-             block_tables=FAKE, context_lens=FAKE, num_seqs=2, num_q_heads=8, num_kv_heads=2, head_dim=128,
-             block_size=16, num_blocks=10, max_blocks_per_seq=4, scale=0.1, dtype=2, partition_size=0,
-             workspace=None, workspace_bytes=0, stream=None)
-    a.update(over)
-    return pkv.load_library().paged_attention_decode_append(*a.values())
-
-
-@pytest.mark.parametrize("over,code", DECODE_BAD + [
-    ({"new_key": None}, pkv.pkv.ERR_INVALID),
-    ({"new_value": None}, pkv.pkv.ERR_INVALID),
-    ({"new_key": FAKE + 8}, pkv.pkv.ERR_INVALID),
-    ({"new_value": FAKE + 4}, pkv.pkv.ERR_INVALID),
-])
-def test_decode_append_rejects_like_decode_and_checks_the_new_tokens(over, code):
-    """Everything paged_attention_decode refuses, plus missing or misaligned new K/V,
-    is refused before any launch (the decode workspace is the same)."""
-    if "workspace" not in over and over.get("partition_size", 0) == 0:
-        over = dict(over, workspace=FAKE, workspace_bytes=1 << 30)
-    assert _decode_append(**over) == code
-    assert pkv.load_library().pkv_last_error()
-
-
-def test_decode_append_empty_batch_is_a_no_op():
-    assert _decode_append(num_seqs=0, out=None, new_key=None) == 0
-
-
 def test_decode_empty_batch_is_a_no_op():
     assert _decode(num_seqs=0, out=None, query=None) == 0
 
