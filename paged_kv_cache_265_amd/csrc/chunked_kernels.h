@@ -244,12 +244,17 @@ __device__ __forceinline__ void chunked_tile(const ChunkedParams& p, int idx, ch
         for (int h = 0; h < 2; ++h)
 #pragma unroll
             for (int ht = 0; ht < NH; ++ht) sc[h][ht] = f32x4{0.f, 0.f, 0.f, 0.f};
+        // the score products at raised wave priority: the matrix cores take this wave's
+        // chain first while the other wave of the SIMD runs its softmax (1-3 % a call).
+        // Not in the mixed launch, where it slows the decode waves sharing the SIMDs.
+        if (!skip_single) __builtin_amdgcn_s_setprio(1);
 #pragma unroll
         for (int ks = 0; ks < KS; ++ks)
 #pragma unroll
             for (int h = 0; h < 2; ++h)
 #pragma unroll
                 for (int ht = 0; ht < NH; ++ht) sc[h][ht] = mma_16x16x32<K>(kf[h][ks], qv[ht][ks], sc[h][ht]);
+        if (!skip_single) __builtin_amdgcn_s_setprio(0);
         // V fragments: head_dim row 16 dt + col, keys 8 gq .. 8 gq + 7 (half gq / 2,
         // chunk gq % 2), read while the first softmax runs
         uint4 vf[DT];
