@@ -238,23 +238,38 @@ __device__ __forceinline__ bool split_range(const DecodeParams& p, long long w, 
                                             bool writer, long long& U_out, long long& lo_out, long long& hi_out,
                                             Cursor& cur) {
     const int NS = p.Hkv * p.chunks;
-    // small batches: sequence 64 j + lane's context and its first unit, in registers
     const bool small = p.S <= kInWaveSeqs;
+    // small batches: lane l holds sequences 4 l .. 4 l + 3, their contexts and first
+    // units in registers (one wave-wide scan over the lanes' tile sums)
     int ctxr[4];
     long long first[4];
-    long long tiles = 0;
+    long long tiles = 0, lane_tiles = 0;
     if (small) {
+        int nbv[4];
+        bool decv[4];
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
-            const int s = 64 * j + lane;
-            const bool dec = s < p.S && is_decode(p, s);
-            ctxr[j] = dec ? p.context_lens[s] : 0;
-            const int nb = ntiles(ctxr[j]);
-            const long long incl = wave_incl_scan((long long)nb, lane);
-            first[j] = (long long)NS * (tiles + incl - nb);
-            tiles += uniform(read_lane64(incl, 63));
-            for (unsigned long long e = __ballot(writer && dec && nb == 0 && s % N_launched == w); e; e &= e - 1) {
-                const int se = 64 * j + __builtin_ctzll(e);
+            const int s = 4 * lane + j;
+            decv[j] = s < p.S && is_decode(p, s);
+            ctxr[j] = decv[j] ? p.context_lens[s] : 0;
+            nbv[j] = ntiles(ctxr[j]);
+            lane_tiles += nbv[j];
+        }
+        const long long incl = wave_incl_scan(lane_tiles, lane);
+        long long run = incl - lane_tiles;  // tiles of the sequences before 4 lane
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            first[j] = (long long)NS * run;
+            run += nbv[j];
+        }
+        tiles = uniform(read_lane64(incl, 63));
+        // zero outputs of the empty decode sequences s with s mod N = w
+        const int nl = (int)N_launched, wi = (int)w;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const int s = 4 * lane + j;
+            for (unsigned long long e = __ballot(writer && decv[j] && nbv[j] == 0 && s % nl == wi); e; e &= e - 1) {
+                const int se = 4 * __builtin_ctzll(e) + j;
                 const size_t n16 = (size_t)p.Hq * p.D * EB / 16;
                 uint4* row = (uint4*)((char*)p.out + row_of_uniform(p, se) * p.Hq * p.D * EB);
                 for (size_t i = lane; i < n16; i += 64) row[i] = make_uint4(0, 0, 0, 0);
@@ -263,7 +278,7 @@ __device__ __forceinline__ bool split_range(const DecodeParams& p, long long w, 
         if (writer && w == 0) {
 #pragma unroll
             for (int j = 0; j < 4; ++j)
-                if (64 * j + lane < p.S) p.starts[64 * j + lane] = first[j];
+                if (4 * lane + j < p.S) p.starts[4 * lane + j] = first[j];
             if (lane == 0) p.starts[p.S] = (long long)NS * tiles;
         }
     }
@@ -285,15 +300,18 @@ __device__ __forceinline__ bool split_range(const DecodeParams& p, long long w, 
     {
         long long a0 = 0;  // first unit of sequence cur.s
         if (small) {
+            // the lane whose sequences hold unit lo, then the sequence among its four
+            const unsigned long long h =
+                __ballot(first[0] <= lo && lo < first[0] + (long long)NS * lane_tiles);
+            const int t = (int)__builtin_ctzll(h);
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
-                const long long units = (long long)NS * ntiles(ctxr[j]);
-                const unsigned long long h = __ballot(first[j] <= lo && lo < first[j] + units);
-                if (h) {
-                    const int t = __builtin_ctzll(h);
-                    cur.s = 64 * j + t;
-                    cur.ctx = read_lane(ctxr[j], t);
-                    a0 = read_lane64(first[j], t);
+                const long long fj = read_lane64(first[j], t);
+                const int cj = read_lane(ctxr[j], t);
+                if (fj <= lo && lo < fj + (long long)NS * ntiles(cj)) {
+                    cur.s = 4 * t + j;
+                    cur.ctx = cj;
+                    a0 = fj;
                     break;
                 }
             }
