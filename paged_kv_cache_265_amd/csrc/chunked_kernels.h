@@ -375,13 +375,24 @@ __device__ __forceinline__ void chunked_tile(const ChunkedParams& p, int idx, ch
     }
 }
 
+// Work item of workgroup i of n: the dispatcher hands workgroup i to XCD i mod 8, and
+// items next to each other share their K/V prefix (the row tiles of one segment and
+// kv head), so each XCD takes a contiguous share of the items and its L2 serves the
+// prefix to all of that share's tiles.
+constexpr int kXcds = 8;
+__device__ __forceinline__ int xcd_item(int i, int n) {
+    const int q = n / kXcds, r = n % kXcds;
+    const int x = i % kXcds, k = i / kXcds;
+    return (x < r ? x * (q + 1) : r * (q + 1) + (x - r) * q) + k;
+}
+
 template <int K, int D, int BS>
 __global__ __launch_bounds__(NW * 64, 2) void chunked_fa(ChunkedParams p) {
     __shared__ __attribute__((aligned(16))) char st0[ChunkLds<D>::STAGE];
     __shared__ __attribute__((aligned(16))) char st1[ChunkLds<D>::STAGE];
     __shared__ __attribute__((aligned(16))) char st2[ChunkLds<D>::STAGE];
     if (contract_broken(p.guard)) return;
-    chunked_tile<K, D, BS>(p, blockIdx.x, st0, st1, st2, false);
+    chunked_tile<K, D, BS>(p, xcd_item((int)blockIdx.x, (int)gridDim.x), st0, st1, st2, false);
 }
 
 }  // namespace
