@@ -375,16 +375,33 @@ __device__ __forceinline__ void chunked_tile(const ChunkedParams& p, int idx, ch
     }
 }
 
-// Work item of workgroup i of n: the dispatcher hands workgroup i to XCD i mod 8, and
-// items next to each other share their K/V prefix (the row tiles of one segment and
-// kv head), so each XCD takes a contiguous share of the items and its L2 serves the
-// prefix to all of that share's tiles.
+// Work items of the chunked grid: n = tiles x P items (P = segments x kv heads, item =
+// pair x tiles + tile); the row tiles of one (segment, kv head) pair share its K/V
+// prefix.  The dispatcher hands workgroup i to XCD i mod 8, so items are renumbered
+// for each XCD's L2 to serve whole pairs:
+//  * xcd_item: each XCD takes a contiguous share of the items (the chunked launch);
+//  * chunk_item: the order runs through the pairs p = r, r + 8, r + 16, ... for
+//    r = 0 .. 7 in turn, a pair's tiles together, and each XCD takes a contiguous share
+//    of that order.  The mixed launch numbers its one-row segments (which return at
+//    once) before the prefill chunks; this spreads the chunks over the XCDs instead of
+//    stacking them onto the last ones.
 constexpr int kXcds = 8;
 __device__ __forceinline__ int xcd_item(int i, int n) {
-    const int q = n / kXcds, r = n % kXcds;
+    const int q = n / kXcds, rem = n % kXcds;
     const int x = i % kXcds, k = i / kXcds;
-    return (x < r ? x * (q + 1) : r * (q + 1) + (x - r) * q) + k;
+    return (x < rem ? x * (q + 1) : rem * (q + 1) + (x - rem) * q) + k;
 }
+__device__ __forceinline__ int chunk_item(int i, int tiles, int P) {
+    int o = xcd_item(i, tiles * P);
+    // position o -> (residue class r, pair, tile)
+    for (int r = 0; r < kXcds; ++r) {
+        const int pairs = (P - r + kXcds - 1) / kXcds;  // pairs p < P with p mod 8 = r
+        if (o < pairs * tiles) return (r + kXcds * (o / tiles)) * tiles + o % tiles;
+        o -= pairs * tiles;
+    }
+    return 0;  // not reached: o < tiles * P
+}
+__device__ __forceinline__ int chunk_tiles(const ChunkedParams& p) { return (p.max_q_len * p.G + ROWS_PER_WG - 1) / ROWS_PER_WG; }
 
 template <int K, int D, int BS>
 __global__ __launch_bounds__(NW * 64, 2) void chunked_fa(ChunkedParams p) {

@@ -37,7 +37,10 @@ __global__ __launch_bounds__(NW * 64, 2) void mixed_kernel(DecodeParams dp, Chun
         const long long w = (long long)blockIdx.x * NW + uniform((int)(threadIdx.x >> 6));
         decode_split_wave<Loop, kMixedRing>(dp, w, (long long)decode_wgs * NW);
     } else {
-        chunked_tile<K, D, BS>(cp, (int)blockIdx.x - decode_wgs, st0, st1, st2, true);
+        // with decode_wgs a multiple of 8 (one per CU) prefill workgroup i sits on XCD
+        // i mod 8, as chunk_item assumes; otherwise only the L2 sharing suffers
+        chunked_tile<K, D, BS>(cp, chunk_item((int)blockIdx.x - decode_wgs, chunk_tiles(cp), cp.Hkv * cp.num_segs), st0,
+                               st1, st2, true);
     }
 }
 
