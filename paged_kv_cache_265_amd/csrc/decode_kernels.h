@@ -215,6 +215,13 @@ __host__ __device__ __forceinline__ long long wave_of(long long u, long long U, 
     return ((u + 1) * N - 1) / U;
 }
 
+// wave_of where a merge finds its pieces: U < N there only with fewer units than
+// kMinWorkingWaves (every unit then a piece of its own), so 32-bit arithmetic serves;
+// otherwise the pieces are the consecutive waves from w0
+__device__ __forceinline__ long long piece_wave(long long w0, long long i, long long a, long long U, long long N) {
+    return U >= N ? w0 + i : (((int)(a + i) + 1) * (int)N - 1) / (int)U;
+}
+
 // ---------------------------------------------------------------------------------------
 // balanced split
 // ---------------------------------------------------------------------------------------
@@ -783,8 +790,7 @@ __global__ __launch_bounds__(kMergeStreamThreads) void decode_merge_stream(Decod
     // record of piece i
     auto record = [&](long long i) -> const float* {
         if (i == 0) return first_rec;
-        const long long w = U >= N ? w0 + i : wave_of(a + i, U, N);
-        return p.ws + (size_t)w * 2 * rec;  // slot 0: that wave's first segment
+        return p.ws + (size_t)piece_wave(w0, i, a, U, N) * 2 * rec;  // slot 0: that wave's first segment
     };
     // one online pass over the pieces, eight at a time: (M, L, O) rescaled by
     // 2^(M_old - M_new)
@@ -848,7 +854,7 @@ __global__ __launch_bounds__(kMergeStreamThreads) void decode_merge_stream(Decod
 // ---------------------------------------------------------------------------------------
 template <int K, int HT, int NG, int DS>
 __global__ __launch_bounds__(NG * 128 / DS) void decode_merge_head(DecodeParams p, int split_waves) {
-    constexpr int kChunk = 16;     // pieces per group in flight at once
+    constexpr int kChunk = NG >= 8 ? 8 : 16;  // pieces per group in flight at once
     constexpr int GL = 128 / DS;   // head_dim lanes of a group
     __shared__ float other[NG - 1][GL + 2];
     if (contract_broken(p.guard)) return;
@@ -891,7 +897,7 @@ __global__ __launch_bounds__(NG * 128 / DS) void decode_merge_head(DecodeParams 
     auto record = [&](long long i) -> const float* {
         if (split_waves == 0) return first + i * rec;
         if (i == 0) return first;
-        return p.ws + (size_t)(U >= N ? w0 + i : wave_of(a + i, U, N)) * 2 * rec;
+        return p.ws + (size_t)piece_wave(w0, i, a, U, N) * 2 * rec;
     };
     const int g = tid / GL, lane = tid - g * GL;
     const int dn = D / DS;             // head_dim elements of this workgroup
