@@ -511,6 +511,10 @@ __global__ __launch_bounds__(64, Loop::kWaves) void decode_split(DecodeParams p)
 // records for the merge, and none when streams and ranges line up.
 // ---------------------------------------------------------------------------------------
 constexpr int kCoopWaves = 4;
+// ring of each cooperative wave: two tiles in flight while one is folded.  Four waves
+// a compute unit with the loop's own six-tile ring kept more bytes in flight than
+// streaming reads gain from (one 131072-token MQA sequence: 30.1 -> 28.3 us with three)
+constexpr int kCoopRing = 3;
 
 // barrier over the workgroup's LDS traffic only: waits for this wave's LDS accesses,
 // not for its global loads still in flight (a release fence would wait for those too)
@@ -1093,7 +1097,7 @@ hipError_t run(const DecodeParams& p0, bool split, bool shallow, int slot, hipSt
             if constexpr (Loop::kCoop) {
                 // one cooperative workgroup (a wave per SIMD) per compute unit
                 waves = (int)std::min<long long>(device_compute_units(), kMaxSplitWaves);
-                hipLaunchKernelGGL((decode_split_coop<Loop, Loop::kRing>), dim3(waves), dim3(64 * kCoopWaves), 0,
+                hipLaunchKernelGGL((decode_split_coop<Loop, kCoopRing>), dim3(waves), dim3(64 * kCoopWaves), 0,
                                    st, p);
             } else {
                 // deep-ring loops are built for one wave per SIMD; the others take what fits
