@@ -239,6 +239,8 @@ def main():
                     help="time the decode call on the same batch with shuffled and with contiguous block "
                          "placement, and with blocks of 8 and 32 tokens, in one process, and print all")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--shape-filter", default=None,
+                    help="--workload shapes: time only the shapes whose label contains this text")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="time a plain 1 GiB device copy (reference kernel for the HBM counters)")
     args = ap.parse_args()
@@ -674,7 +676,7 @@ def run_shapes(args, torch, pkv, workloads, dev):
     from workloads.gen import make_decode_case
     rows = []
     import numpy as np
-    only = getattr(args, "shape_filter", None)
+    only = args.shape_filter
     for i, (label, dt, ctx, hq, hkv) in enumerate(SHAPES):
         if only and only not in label:
             continue
