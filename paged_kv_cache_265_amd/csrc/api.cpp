@@ -489,7 +489,7 @@ int paged_attention_mixed(void* out, const void* query, const int32_t* cu_q_lens
     d.part_tokens = 0;
     d.max_parts = 0;
     d.scale_log2 = c.scale_log2;
-    hipError_t e = pkv::launch_mixed(d, c, dtype, (hipStream_t)stream);
+    hipError_t e = pkv::launch_mixed(d, c, dtype, (long long)total_q - num_segs, (hipStream_t)stream);
     if (e != hipSuccess) return hip_fail(e, fn);
     return finish_checked(fn, dbg);
 }

@@ -117,7 +117,9 @@ hipError_t launch_decode_bs32(const DecodeParams& p, int kind, int path, int rin
 hipError_t launch_chunked(const ChunkedParams& p, int kind, hipStream_t stream);
 // one launch for a flattened batch: the one-row segments of cp through the decode
 // split described by dp (dp.cu_q = cp.cu_q_lens), the others as chunked tiles
-hipError_t launch_mixed(const DecodeParams& dp, const ChunkedParams& cp, int kind, hipStream_t stream);
+// (prefill_rows: total_q - num_segs, the rows past the first of every segment)
+hipError_t launch_mixed(const DecodeParams& dp, const ChunkedParams& cp, int kind, long long prefill_rows,
+                        hipStream_t stream);
 hipError_t launch_reshape_and_cache(const CacheParams& p, int kind, hipStream_t stream);
 hipError_t launch_copy_blocks(const CopyParams& p, int num_layers, hipStream_t stream);
 hipError_t launch_read_probe(const void* buf, size_t bytes, void* sink, hipStream_t stream);

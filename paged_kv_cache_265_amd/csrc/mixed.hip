@@ -28,7 +28,8 @@ namespace {
 constexpr int kMixedRing = 3;
 
 template <class Loop, int K, int D, int BS>
-__global__ __launch_bounds__(NW * 64, 2) void mixed_kernel(DecodeParams dp, ChunkedParams cp, int decode_wgs) {
+__global__ __launch_bounds__(NW * 64, 2) void mixed_kernel(DecodeParams dp, ChunkedParams cp, int decode_wgs,
+                                                            int by_pair) {
     __shared__ __attribute__((aligned(16))) char st0[ChunkLds<D>::STAGE];
     __shared__ __attribute__((aligned(16))) char st1[ChunkLds<D>::STAGE];
     __shared__ __attribute__((aligned(16))) char st2[ChunkLds<D>::STAGE];
@@ -39,13 +40,14 @@ __global__ __launch_bounds__(NW * 64, 2) void mixed_kernel(DecodeParams dp, Chun
     } else {
         // with decode_wgs a multiple of 8 (one per CU) prefill workgroup i sits on XCD
         // i mod 8, as chunk_item assumes; otherwise only the L2 sharing suffers
-        chunked_tile<K, D, BS>(cp, chunk_item((int)blockIdx.x - decode_wgs, chunk_tiles(cp), cp.Hkv * cp.num_segs), st0,
-                               st1, st2, true);
+        const int i = (int)blockIdx.x - decode_wgs;
+        chunked_tile<K, D, BS>(cp, by_pair ? chunk_item(i, chunk_tiles(cp), cp.Hkv * cp.num_segs) : i, st0, st1, st2,
+                               true);
     }
 }
 
 template <class Loop, int K, int D, int BS>
-hipError_t go(const DecodeParams& dp0, const ChunkedParams& cp, hipStream_t st) {
+hipError_t go(const DecodeParams& dp0, const ChunkedParams& cp, long long prefill_rows, hipStream_t st) {
     DecodeParams dp = dp0;
     dp.chunks = (dp.G + Loop::HT - 1) / Loop::HT;
     const int NS = dp.Hkv * dp.chunks;
@@ -54,10 +56,18 @@ hipError_t go(const DecodeParams& dp0, const ChunkedParams& cp, hipStream_t st) 
     if (decode_wgs * NW > kMaxSplitWaves) decode_wgs = kMaxSplitWaves / NW;
     const long long tiles = ((long long)cp.max_q_len * cp.G + ROWS_PER_WG - 1) / ROWS_PER_WG;
     const long long grid = decode_wgs + tiles * cp.Hkv * cp.num_segs;
+    // Whole (segment, kv head) pairs per XCD (chunk_item) only when there are surely at
+    // least as many prefill pairs as XCDs: a chunk holds at most max_q_len - 1 of the
+    // prefill_rows, so there are at least prefill_rows / (max_q_len - 1) chunks.  With
+    // fewer, whole pairs would leave XCDs without prefill work (two 512-row chunks beside
+    // long MQA decode: 0.44 ms against 0.26 ms with every pair's tiles spread over all
+    // XCDs in launch order), so the tiles go in launch order instead.
+    const long long min_chunks = cp.max_q_len > 1 ? (prefill_rows + cp.max_q_len - 2) / (cp.max_q_len - 1) : 0;
+    const int by_pair = min_chunks * cp.Hkv >= kXcds ? 1 : 0;
     if (dp.S > kInWaveSeqs)
         hipLaunchKernelGGL((decode_split_prologue<Loop::kElemBytes>), dim3(1), dim3(kPrologueThreads), 0, st, dp, NS);
     hipLaunchKernelGGL((mixed_kernel<Loop, K, D, BS>), dim3((unsigned)grid), dim3(NW * 64), 0, st, dp, cp,
-                       decode_wgs);
+                       decode_wgs, by_pair);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     const int waves = decode_wgs * NW;
@@ -69,31 +79,32 @@ hipError_t go(const DecodeParams& dp0, const ChunkedParams& cp, hipStream_t st) 
 // decode inner loop as in paged_attention_decode: the vector ALU for one or two
 // query heads per kv head, the matrix cores otherwise
 template <int K, int D, int BS>
-hipError_t pick(const DecodeParams& dp, const ChunkedParams& cp, hipStream_t st) {
-    if (dp.G == 1) return go<ValuLoop<K, D, 1, BS>, K, D, BS>(dp, cp, st);
-    if (dp.G == 2) return go<ValuLoop<K, D, 2, BS>, K, D, BS>(dp, cp, st);
-    if (dp.G <= 16) return go<MfmaLoop<K, D, 1, BS>, K, D, BS>(dp, cp, st);
-    return go<MfmaWideLoop<K, D, BS>, K, D, BS>(dp, cp, st);
+hipError_t pick(const DecodeParams& dp, const ChunkedParams& cp, long long prefill_rows, hipStream_t st) {
+    if (dp.G == 1) return go<ValuLoop<K, D, 1, BS>, K, D, BS>(dp, cp, prefill_rows, st);
+    if (dp.G == 2) return go<ValuLoop<K, D, 2, BS>, K, D, BS>(dp, cp, prefill_rows, st);
+    if (dp.G <= 16) return go<MfmaLoop<K, D, 1, BS>, K, D, BS>(dp, cp, prefill_rows, st);
+    return go<MfmaWideLoop<K, D, BS>, K, D, BS>(dp, cp, prefill_rows, st);
 }
 
 template <int K, int D>
-hipError_t by_block_size(const DecodeParams& dp, const ChunkedParams& cp, hipStream_t st) {
+hipError_t by_block_size(const DecodeParams& dp, const ChunkedParams& cp, long long prefill_rows, hipStream_t st) {
     switch (dp.BS) {
-    case 8: return pick<K, D, 8>(dp, cp, st);
-    case 16: return pick<K, D, 16>(dp, cp, st);
-    case 32: return pick<K, D, 32>(dp, cp, st);
+    case 8: return pick<K, D, 8>(dp, cp, prefill_rows, st);
+    case 16: return pick<K, D, 16>(dp, cp, prefill_rows, st);
+    case 32: return pick<K, D, 32>(dp, cp, prefill_rows, st);
     default: return hipErrorInvalidValue;
     }
 }
 
 }  // namespace
 
-hipError_t launch_mixed(const DecodeParams& dp, const ChunkedParams& cp, int kind, hipStream_t st) {
+hipError_t launch_mixed(const DecodeParams& dp, const ChunkedParams& cp, int kind, long long prefill_rows,
+                        hipStream_t st) {
     switch (kind * 1000 + dp.D) {
-    case KF16 * 1000 + 64: return by_block_size<KF16, 64>(dp, cp, st);
-    case KF16 * 1000 + 128: return by_block_size<KF16, 128>(dp, cp, st);
-    case KBF16 * 1000 + 64: return by_block_size<KBF16, 64>(dp, cp, st);
-    case KBF16 * 1000 + 128: return by_block_size<KBF16, 128>(dp, cp, st);
+    case KF16 * 1000 + 64: return by_block_size<KF16, 64>(dp, cp, prefill_rows, st);
+    case KF16 * 1000 + 128: return by_block_size<KF16, 128>(dp, cp, prefill_rows, st);
+    case KBF16 * 1000 + 64: return by_block_size<KBF16, 64>(dp, cp, prefill_rows, st);
+    case KBF16 * 1000 + 128: return by_block_size<KBF16, 128>(dp, cp, prefill_rows, st);
     default: return hipErrorInvalidValue;
     }
 }

@@ -80,6 +80,11 @@ CASES = [
     # more segments than one round of in-wave loads: the decode start units come from
     # the prologue's scan
     ("bf16", 8, 1, 128, [40 + (i * 53) % 900 for i in range(300)] + [700, 0], [1] * 300 + [33, 64]),
+    # at least eight (chunk, kv head) pairs for sure (the launch then gives each XCD whole
+    # pairs; the cases above have fewer and take the tiles in launch order): eight kv
+    # heads with one chunk, one kv head with eight chunks
+    ("bf16", 4, 8, 128, [30, 200, 1000], [1, 40, 1]),
+    ("bf16", 32, 1, 128, [100, 3000] + [50 + 37 * i for i in range(8)], [1, 1] + [9] * 8),
 ]
 
 
