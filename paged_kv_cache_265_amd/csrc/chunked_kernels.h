@@ -384,7 +384,8 @@ __device__ __forceinline__ void chunked_tile(const ChunkedParams& p, int idx, ch
 //    r = 0 .. 7 in turn, a pair's tiles together, and each XCD takes a contiguous share
 //    of that order.  The mixed launch numbers its one-row segments (which return at
 //    once) before the prefill chunks; this spreads the chunks over the XCDs instead of
-//    stacking them onto the last ones.
+//    stacking them onto the last ones, as long as there are at least eight prefill
+//    pairs (with fewer, the mixed launch keeps launch order).
 constexpr int kXcds = 8;
 __device__ __forceinline__ int xcd_item(int i, int n) {
     const int q = n / kXcds, rem = n % kXcds;
