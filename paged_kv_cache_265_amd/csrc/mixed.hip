@@ -17,7 +17,7 @@
 // of split decode streams runs as a second, small launch.
 //
 // The whole kernel is sized for two workgroups (two waves per SIMD) per compute
-// unit, the chunked tiles' budget; the decode waves run a three-tile ring.
+// unit, the chunked tiles' budget; the decode waves run a two-tile ring.
 #include "chunked_kernels.h"
 #include "decode_kernels.h"
 
@@ -25,7 +25,11 @@ namespace pkv {
 
 namespace {
 
-constexpr int kMixedRing = 3;
+// the decode waves' ring: one tile in flight while one is folded.  Fewer decode loads in
+// flight per CU leave the memory pipeline to the prefill tiles' K/V loads beside them
+// (two 512-row chunks beside long MQA decode: 275 -> 266 us; one chunk beside the GQA
+// batch: 336 -> 328 us; a four-tile ring was slower)
+constexpr int kMixedRing = 2;
 
 template <class Loop, int K, int D, int BS>
 __global__ __launch_bounds__(NW * 64, 2) void mixed_kernel(DecodeParams dp, ChunkedParams cp, int decode_wgs,
