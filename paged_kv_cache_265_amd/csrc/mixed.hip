@@ -55,8 +55,15 @@ hipError_t go(const DecodeParams& dp0, const ChunkedParams& cp, long long prefil
     DecodeParams dp = dp0;
     dp.chunks = (dp.G + Loop::HT - 1) / Loop::HT;
     const int NS = dp.Hkv * dp.chunks;
-    // one decode workgroup (four waves: one per SIMD) per compute unit
+    // one decode workgroup (four waves: one per SIMD) per compute unit -- per two compute
+    // units for the 32-head loop when the prefill tiles with rows (about prefill_rows x
+    // Hq / ROWS_PER_WG) alone fill a slot on every unit: those decode waves keep the SIMDs
+    // busier than the 16-head loop's, and the prefill tiles beside them get more room
+    // (long MQA batch with eight 512-row chunks: 0.455 -> 0.443 ms; the GQA batch with
+    // eight chunks, where the 16-head loop decodes, lost 4 % the same way)
     int decode_wgs = device_compute_units();
+    if (Loop::kCoop && prefill_rows * cp.Hq >= (long long)decode_wgs * ROWS_PER_WG && decode_wgs >= 16)
+        decode_wgs = decode_wgs / 16 * 8;
     if (decode_wgs * NW > kMaxSplitWaves) decode_wgs = kMaxSplitWaves / NW;
     const long long tiles = ((long long)cp.max_q_len * cp.G + ROWS_PER_WG - 1) / ROWS_PER_WG;
     const long long grid = decode_wgs + tiles * cp.Hkv * cp.num_segs;
